@@ -1,0 +1,267 @@
+"""Benchmark: sink + window attention on one MI355X (Wan-1.3B-shaped layer, bf16).
+
+One step = one latent frame of one layer in steady state, the whole hot path:
+  sa_cache_append  (K rotated at the frame's time and written to its ring slot,
+                    V written transposed; the oldest local frame is evicted)
+  sa_window_attn   (the frame's 1560 queries, rotated on load, attend over
+                    3 sink + 9 local frames = 18720 keys, 12 heads, D = 128).
+Steps cycle over 8 independent layer caches (8 x 115 MB, larger than the
+256 MB last-level cache) so K/V come from HBM as in a real layer stack.
+
+The KV recache (prompt switch, M = 18720 tokens, N = 2 x 1536, K = 1536) and
+the standalone RoPE are timed in the same run and reported beside the step.
+
+value = attention algorithmic TFLOP/s of the whole step (4 H D per visible
+query-key pair = 179.42 GFLOP per frame; the append's time counts, its bytes
+add no flops).  roofline.achieved uses the attention kernel's own time from
+HIP events around each call on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (vendor figure)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+N_LAYERS = 8
+
+
+def attn_flops(n_q_rows: int, n_keys: int, H: int, D: int) -> float:
+    return 4.0 * H * D * n_q_rows * n_keys
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per attention launch from the committed counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "attn_bf16_wan13b_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if vals.get("kernel_source_sha256_16") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle as it stands, on a bounded sample of one steady-state step."""
+    import numpy as np
+    import workloads as wl
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+    from oracle import rope as orope
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    T = w.tokens_per_frame
+    f = 20
+    res = ocache.resident_frames(f + 1, w.n_sink, w.n_local)
+    bases = orope.theta_hat(w.theta0, w.sigma, np.zeros(w.n_heads))
+    kf, vf = [], []
+    for r in res:
+        kf.append(wl.frame_qkv(w, r, tensor=wl.TENSOR_K))
+        vf.append(wl.frame_qkv(w, r, tensor=wl.TENSOR_V))
+    q = wl.frame_qkv(w, f, tensor=wl.TENSOR_Q)
+    t0 = time.perf_counter()
+    # append: rotate the new frame's keys; attend: rotate q, attention head by head
+    kf_rot = [orope.rope3d_frame(k, r, bases, w.dims, w.grid[1]) for k, r in zip(kf, res)]
+    q_rot = orope.rope3d_frame(q, f, bases, w.dims, w.grid[1])
+    heads_done = 0
+    for h in range(w.n_heads):
+        oattn.window_attention(q_rot, kf_rot, vf, res, [f], T, True, heads=[h])
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = attn_flops(T, len(res) * T, heads_done, w.head_dim)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one steady-state frame (1560 queries x 18720 keys), {heads_done} of {w.n_heads} heads, "
+                      f"fp64 numpy incl. RoPE of all 12 cached frames; {dt:.1f} s",
+            "latent_frames_per_s_per_layer": (heads_done / w.n_heads) / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sink_window_kv_amd as swk
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[2]
+    T, H, D = w.tokens_per_frame, w.n_heads, w.head_dim
+    n_win = w.n_sink + w.n_local
+    bf = torch.bfloat16
+    print(f"[bench] {w.name}: preparing {N_LAYERS} layer caches", file=sys.stderr, flush=True)
+
+    pool = 16  # distinct seeded frames, reused round-robin
+    qs, ks, vs = [], [], []
+    for f in range(pool):
+        qs.append(torch.from_numpy(wl.frame_qkv(w, f, tensor=wl.TENSOR_Q)).to(dev, bf).contiguous())
+        ks.append(torch.from_numpy(wl.frame_qkv(w, f, tensor=wl.TENSOR_K)).to(dev, bf).contiguous())
+        vs.append(torch.from_numpy(wl.frame_qkv(w, f, tensor=wl.TENSOR_V)).to(dev, bf).contiguous())
+    rope = swk.Rope(H, D, w.dims, w.grid, w.theta0, w.sigma, None)
+    caches = [swk.Cache(rope, 1, w.n_sink, w.n_local, bf, device=dev) for _ in range(N_LAYERS)]
+    t_next = [0] * N_LAYERS
+    for li, c in enumerate(caches):
+        for f in range(n_win):
+            swk.sa_cache_append(c, ks[(f + li) % pool], vs[(f + li) % pool], 1, t_next[li])
+            t_next[li] += 1
+    ws_bytes = max(swk.sa_window_attn_workspace(c, 1) for c in caches)
+    ws = torch.zeros(max(ws_bytes // 4, 4), dtype=torch.float32, device=dev)
+    o = torch.empty_like(qs[0])
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        li = i % N_LAYERS
+        c = caches[li]
+        fi = (t_next[li] + li) % pool
+        if ev is not None:
+            ev[0].record(stream)
+        swk.sa_cache_append(c, ks[fi], vs[fi], 1, t_next[li])
+        if ev is not None:
+            ev[1].record(stream)
+        swk.sa_window_attn(c, qs[fi], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        t_next[li] += 1
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    # Timed region: whole steps, no events in the way.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # Same loop again with HIP events on the launch stream: per-kernel durations.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    app_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    att_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    app_avg = sum(app_ms) / len(app_ms)
+    att_avg = sum(att_ms) / len(att_ms)
+
+    flops = attn_flops(T, n_win * T, H, D)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (att_avg * 1e-3) / 1e12
+    append_bytes = 2 * 2 * T * H * D * 2  # K and V, read + write, bf16
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us, attention {att_avg * 1e3:.1f} us "
+          f"({achieved:.0f} TFLOP/s), append {app_avg * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # Standalone RoPE (Q of one frame, read + write) and the KV recache.
+    qrot = torch.empty_like(qs[0])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(5):
+        swk.sa_rope3d_apply(rope, qs[0], qrot, 1, 1, 123)
+    e0.record(stream)
+    for _ in range(50):
+        swk.sa_rope3d_apply(rope, qs[0], qrot, 1, 1, 123)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rope_us = e0.elapsed_time(e1) * 1e3 / 50
+    rope_bytes = 2 * T * H * D * 2
+
+    w4 = wl.WORKLOADS[4]
+    x, wk, wv = wl.recache_inputs(w4)
+    tx = torch.from_numpy(x).to(dev, bf).contiguous()
+    twk = torch.from_numpy(np.ascontiguousarray(wk.T)).to(dev, bf).contiguous()
+    twv = torch.from_numpy(np.ascontiguousarray(wv.T)).to(dev, bf).contiguous()
+    rc = caches[0]
+    for _ in range(3):
+        swk.sa_cache_recache(rc, tx, twk, twv, w4.hidden)
+    e0.record(stream)
+    n_rc = 20
+    for _ in range(n_rc):
+        swk.sa_cache_recache(rc, tx, twk, twv, w4.hidden)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rc_us = e0.elapsed_time(e1) * 1e3 / n_rc
+    rc_flops = 2.0 * (n_win * T) * (2 * H * D) * w4.hidden
+    rc_bytes = (n_win * T * w4.hidden + 2 * H * D * w4.hidden + 2 * n_win * T * H * D) * 2
+
+    traffic = traffic_from_profile(os.path.join(ROOT, "sink_window_kv_amd", "csrc", "window_attn.hip"))
+    out = {
+        "metric": "sink+window attn TFLOP/s & latent frames/s/layer on 1 MI355X; % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(128) Q, K, V in bf16; no model weights)",
+        "config": {"workload": "wan13b-layer-bf16: B=1, H=12, D=128 (RoPE 44/42/42), 30x52=1560 tokens/frame, "
+                               "3 sink + 9 local = 18720 keys, 1 query frame, sigma=0; step = append + attend, "
+                               "8 layer caches cycled",
+                   "layers_cycled": N_LAYERS, "tokens_per_frame": T, "keys": n_win * T},
+        "latent_frames_per_s_per_layer": round(1e3 / ms_per_step, 1),
+        "attention_only_latent_frames_per_s_per_layer": round(1e3 / att_avg, 1),
+        "pct_bf16_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_bf16_peak_attention_kernel": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_bf16_kernel<128>",
+                     "flops_per_launch": flops, "avg_launch_us": round(att_avg * 1e3, 2),
+                     "median_launch_us": round(att_ms[len(att_ms) // 2] * 1e3, 2)},
+        "append": {"avg_us": round(app_avg * 1e3, 2), "bytes": append_bytes,
+                   "GBps": round(append_bytes / (app_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBPS},
+        "rope3d_q": {"avg_us": round(rope_us, 2), "bytes": rope_bytes,
+                     "GBps": round(rope_bytes / (rope_us * 1e-6) / 1e9, 1)},
+        "recache": {"avg_us": round(rc_us, 1), "flops": rc_flops,
+                    "TFLOPs": round(rc_flops / (rc_us * 1e-6) / 1e12, 1),
+                    "pct_bf16_peak": round(100.0 * rc_flops / (rc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                    "min_bytes": rc_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

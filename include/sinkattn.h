@@ -1,0 +1,219 @@
+/*
+ * libsinkattn -- frame-sink + short-window KV attention for one MI355X (gfx950).
+ *
+ * The operations follow two reviewed papers:
+ *   [LongLive]  "LongLive: Real-time Interactive Long Video Generation",
+ *               paper review page (xllm-io paper-review blog).
+ *   [LoL]       "LoL: Longer than Longer, Scaling Video Generation to Hour",
+ *               paper review page (rainbus paper reviews).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors crossing the boundary are dense, row-major, in the [B, T, H, D]
+ *   token-major layout the LoL review states for Q and K ("method steps" (1)):
+ *   B streams, T tokens (latent frames x tokens per frame), H heads, D channels.
+ *   Token i of a latent frame sits at grid row i / grid_w, column i % grid_w.
+ * - Device pointers are plain device addresses (hipMalloc / torch CUDA
+ *   tensors); host pointers are marked "host".  The library never frees or
+ *   keeps a caller pointer beyond the call, except the two cache stores named
+ *   in sa_cache_desc, which it borrows for the cache handle's lifetime.
+ * - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *   stream).  Every launch is asynchronous on that stream; no call
+ *   synchronises the host except sa_rope_create (one table upload).
+ * - Element types: SA_BF16 (bfloat16, round-to-nearest-even on every store)
+ *   or SA_F32.  All arithmetic is fp32 (bf16 MFMA inputs, fp32 accumulation);
+ *   RoPE angles are formed and range-reduced in fp64.
+ * - Every function returns an sa_status.  Arguments and state are validated
+ *   before anything is changed or launched: on error the handle is left as it
+ *   was and sa_last_error() (thread-local) describes the problem.
+ *   SA_ERR_HIP reports a HIP runtime / launch error; device faults surface at
+ *   the caller's next synchronisation.
+ * - Handles are not thread-safe; distinct handles are independent.  A handle
+ *   is bound to the device that was current at its creation.
+ * - Alignment: every device pointer must be 16-byte aligned.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,   /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,  /* sizes inconsistent or unsupported */
+  SA_ERR_DTYPE = 3,  /* element type unsupported or mismatched */
+  SA_ERR_ALIGN = 4,  /* pointer not 16-byte aligned */
+  SA_ERR_STATE = 5,  /* the cache cannot do this now (e.g. attend on an empty cache) */
+  SA_ERR_RANGE = 6,  /* a value is out of range (positions, chunk size, workspace) */
+  SA_ERR_HIP = 7     /* HIP runtime or launch failure */
+} sa_status;
+
+typedef enum { SA_BF16 = 0, SA_F32 = 1 } sa_dtype;
+
+/* Attention mask inside a multi-frame query chunk.
+ * SA_MASK_NONE: every query sees every resident frame.
+ * SA_MASK_FRAME_CAUSAL: a query of latent frame f sees the resident frames
+ * f' <= f in full (frame-level autoregression, [LongLive] section 2 "solution
+ * overview"; chunk-wise generation compared in section 5's table). */
+typedef enum { SA_MASK_NONE = 0, SA_MASK_FRAME_CAUSAL = 1 } sa_mask;
+
+#define SA_AXIS_T 1u
+#define SA_AXIS_H 2u
+#define SA_AXIS_W 4u
+#define SA_MAX_FRAMES 64 /* n_sink + n_local */
+
+/* ------------------------------------------------------------------ RoPE --
+ * 3D rotary position embedding with LoL's per-head jittered base.
+ * [LoL] background "Rotary Position Embedding": channel pair p at position pos
+ *   is rotated by R(phi) = [[cos phi, -sin phi], [sin phi, cos phi]],
+ *   phi = pos * w_p, w = base^(-2j/d).
+ * [LoL] "method steps" (2)-(7): per head h, theta_hat_h = theta0 (1 + sigma eps_h),
+ *   eps_h ~ U[-1, 1] drawn by the caller (the library has no RNG).
+ * Layout of the head dimension: adjacent pairs (2p, 2p+1); consecutive
+ * segments [t | h | w] of dim_t, dim_h, dim_w channels; segment a uses
+ * w_{a,j} = base_a^(-2j/dim_a), j = 0 .. dim_a/2 - 1, with base_a =
+ * theta_hat_h on jittered axes (jitter_axes bitmask) and theta0 elsewhere.
+ * Positions: t = the latent frame's time index; h = token / grid_w;
+ * w = token % grid_w.
+ */
+typedef struct {
+  int32_t n_heads;      /* H >= 1 */
+  int32_t head_dim;     /* D in {64, 128} */
+  int32_t dim_t, dim_h, dim_w; /* even, sum = D */
+  int32_t grid_h, grid_w;      /* tokens per latent frame = grid_h * grid_w, a multiple of 8 */
+  double theta0;        /* > 1 */
+  double sigma;         /* jitter scale, >= 0; every theta_hat must stay > 1 */
+  const double* eps;    /* host [H], each in [-1, 1]; NULL = no jitter; copied */
+  uint32_t jitter_axes; /* SA_AXIS_* bitmask; 0 is treated as SA_AXIS_T */
+} sa_rope_desc;
+
+typedef struct sa_rope sa_rope;
+
+/* Host-only: per-head bases theta_hat [H*3] (t, h, w) and frequencies
+ * w [H*D/2] in fp64, as the device tables will hold them.  No HIP call; either
+ * output may be NULL. */
+sa_status sa_rope_tables(const sa_rope_desc* desc, double* theta_hat_out, double* freq_out);
+
+/* Validates desc, builds the fp64 frequency table and uploads it to the
+ * current device (the only allocating / synchronising call of the library
+ * besides this handle's destroy). */
+sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out);
+void sa_rope_destroy(sa_rope* rope);
+
+/* y = RoPE(x) for n_frames latent frames: x, y [B, n_frames*T_f, H, D] of
+ * dtype; frame j of the token axis has time t0 + j.  y may alias x exactly. */
+sa_status sa_rope3d_apply(const sa_rope* rope, const void* x, void* y, sa_dtype dtype,
+                          int32_t batch, int32_t n_frames, int64_t t0, void* stream);
+
+/* ----------------------------------------------------------------- cache --
+ * [LongLive] section 3 "Frame Sink" and "Short-Window Attention": the KV of
+ * the first n_sink latent frames is pinned for the whole stream; the other
+ * frames live in a local window of the n_local most recent frames (the paper
+ * uses 3 sink + 9 local = 12 frames, section 6 implementation table).
+ * Frame f < n_sink goes to sink slot f; frame f >= n_sink to ring slot
+ * (f - n_sink) mod n_local, evicting the frame that held it.
+ * Logical order = sinks, then local frames oldest -> newest.
+ *
+ * Storage (library-internal layout, caller-allocated, borrowed):
+ *   k_store: [n_sink + n_local][B][H][T_f][D]   keys, rotated at their frame time
+ *   v_store: [n_sink + n_local][B][H][D][T_f]   values, transposed per (slot, b, h)
+ * Each store is sa_cache_store_bytes(desc) bytes.  Use sa_cache_read to view a
+ * frame in the boundary layout.
+ */
+typedef struct {
+  int32_t batch;            /* B >= 1 */
+  int32_t n_heads;          /* must equal the rope's */
+  int32_t head_dim;         /* must equal the rope's */
+  int32_t tokens_per_frame; /* must equal the rope's grid_h * grid_w */
+  int32_t n_sink;           /* >= 0 */
+  int32_t n_local;          /* >= 1, n_sink + n_local <= SA_MAX_FRAMES */
+  sa_dtype dtype;
+  void* k_store;            /* device */
+  void* v_store;            /* device */
+} sa_cache_desc;
+
+typedef struct sa_cache sa_cache;
+
+typedef struct {
+  int64_t frame;   /* frame number (0-based count of appended frames) */
+  int64_t t;       /* time position the key was rotated with */
+  int32_t segment; /* 0 sink, 1 ring */
+  int32_t slot;    /* index inside its segment */
+} sa_slot;
+
+/* Bytes of ONE store (k or v) for desc; 0 if desc is invalid. */
+size_t sa_cache_store_bytes(const sa_cache_desc* desc);
+
+/* Host metadata only; makes no HIP call.  rope must outlive the cache. */
+sa_status sa_cache_create(const sa_cache_desc* desc, const sa_rope* rope, sa_cache** out);
+void sa_cache_destroy(sa_cache* cache);
+
+/* Forget every frame (the "no KV cache" policy at a prompt switch,
+ * [LongLive] section 3 "KV Recache", strategy comparison). */
+sa_status sa_cache_reset(sa_cache* cache);
+
+/* Append n_frames latent frames (a chunk) with times t0 .. t0+n_frames-1:
+ * k, v [B, n_frames*T_f, H, D] un-rotated.  K is rotated at each frame's t and
+ * stored; V is stored transposed.  Requires t0 > the newest cached t and the
+ * chunk's non-sink frames to fit the ring (<= n_local), so a chunk never
+ * evicts its own frames (SA_ERR_RANGE otherwise). */
+sa_status sa_cache_append(sa_cache* cache, const void* k, const void* v, int32_t n_frames,
+                          int64_t t0, void* stream);
+
+/* KV recache at a prompt switch ([LongLive] section 3 "KV Recache"): for every
+ * resident frame, K = RoPE(x . W_k, t_frame), V = x . W_v, written in place;
+ * slots, order and times are unchanged.
+ *   x    [B, n_resident*T_f, hidden]  hidden states of the resident frames in
+ *                                     logical order (sinks, then local oldest -> newest)
+ *   w_k, w_v [H*D, hidden]            projection weights in the nn.Linear
+ *                                     [out, in] layout: row h*D+d makes channel d of head h
+ * All of the cache's dtype.  hidden must be a multiple of 64.  SA_ERR_STATE on
+ * an empty cache. */
+sa_status sa_cache_recache(sa_cache* cache, const void* x, const void* w_k, const void* w_v,
+                           int32_t hidden, void* stream);
+
+/* Workspace sa_window_attn needs for this cache state and n_q (may be 0). */
+sa_status sa_window_attn_workspace(const sa_cache* cache, int32_t n_q, size_t* bytes);
+
+/* Sink + window attention ([LongLive] section 3 "Short-Window Attention"
+ * equation; [LoL] background "multi-head attention" equation):
+ *   o = softmax(RoPE(q) K^T * scale) V per (stream, head), over the resident
+ *   frames (all of them, or frame-causally with SA_MASK_FRAME_CAUSAL).
+ *   q, o  [B, n_q*T_f, H, D]: un-rotated queries of the NEWEST n_q resident
+ *         frames (append first, then attend); q is rotated at those frames' t.
+ *   scale 0 => 1/sqrt(D).
+ *   workspace: device scratch of at least sa_window_attn_workspace() bytes
+ *         (NULL allowed when that is 0); SA_ERR_RANGE if too small.  It must
+ *         be zero-filled before its first use; every call leaves its first
+ *         4096 bytes (arrival counters) zero again, so one workspace serves
+ *         any number of calls and shapes.  Calls sharing a workspace must not
+ *         run concurrently (stream order is enough).
+ * o must not alias q. */
+sa_status sa_window_attn(const sa_cache* cache, const void* q, void* o, int32_t n_q, float scale,
+                         sa_mask mask, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Resident frames in logical order (host, no sync): writes min(cap, n) entries,
+ * *n_valid = n. */
+sa_status sa_cache_slots(const sa_cache* cache, sa_slot* out, int32_t cap, int32_t* n_valid);
+
+/* Copy logical frame `index` out in the boundary layout: k_out, v_out
+ * [B, T_f, H, D] (either may be NULL).  K as stored (rotated). */
+sa_status sa_cache_read(const sa_cache* cache, int32_t index, void* k_out, void* v_out,
+                        void* stream);
+
+/* Number of frames appended since creation / reset, and resident now. */
+sa_status sa_cache_counts(const sa_cache* cache, int64_t* n_appended, int32_t* n_resident);
+
+const char* sa_status_str(sa_status status);
+const char* sa_last_error(void); /* thread-local, "" when none */
+const char* sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SINKATTN_H */

@@ -1,0 +1,273 @@
+"""Python binding of libsinkattn (ctypes; argument marshalling only).
+
+The functions keep the C names (``sa_rope_create``, ``sa_cache_append``,
+``sa_window_attn`` ...) and take torch CUDA tensors for device buffers;
+every step runs in the HIP library.  PyTorch only supplies device memory
+and the current stream.  There is no CPU fallback: if the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libsinkattn.so")
+
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_ALIGN, SA_ERR_STATE, SA_ERR_RANGE, SA_ERR_HIP = range(8)
+SA_BF16, SA_F32 = 0, 1
+SA_MASK_NONE, SA_MASK_FRAME_CAUSAL = 0, 1
+SA_AXIS_T, SA_AXIS_H, SA_AXIS_W = 1, 2, 4
+SA_MAX_FRAMES = 64
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE",
+                 4: "SA_ERR_ALIGN", 5: "SA_ERR_STATE", 6: "SA_ERR_RANGE", 7: "SA_ERR_HIP"}
+
+
+class sa_rope_desc(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dim_t", ctypes.c_int32), ("dim_h", ctypes.c_int32), ("dim_w", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("theta0", ctypes.c_double), ("sigma", ctypes.c_double),
+                ("eps", ctypes.POINTER(ctypes.c_double)), ("jitter_axes", ctypes.c_uint32)]
+
+
+class sa_cache_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("tokens_per_frame", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+                ("n_local", ctypes.c_int32), ("dtype", ctypes.c_int), ("k_store", ctypes.c_void_p),
+                ("v_store", ctypes.c_void_p)]
+
+
+class sa_slot(ctypes.Structure):
+    _fields_ = [("frame", ctypes.c_int64), ("t", ctypes.c_int64), ("segment", ctypes.c_int32),
+                ("slot", ctypes.c_int32)]
+
+
+_VP = ctypes.c_void_p
+_SIGNATURES = {
+    "sa_rope_tables": (ctypes.c_int, [ctypes.POINTER(sa_rope_desc), ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_double)]),
+    "sa_rope_create": (ctypes.c_int, [ctypes.POINTER(sa_rope_desc), ctypes.POINTER(_VP)]),
+    "sa_rope_destroy": (None, [_VP]),
+    "sa_rope3d_apply": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int64, _VP]),
+    "sa_cache_store_bytes": (ctypes.c_size_t, [ctypes.POINTER(sa_cache_desc)]),
+    "sa_cache_create": (ctypes.c_int, [ctypes.POINTER(sa_cache_desc), _VP, ctypes.POINTER(_VP)]),
+    "sa_cache_destroy": (None, [_VP]),
+    "sa_cache_reset": (ctypes.c_int, [_VP]),
+    "sa_cache_append": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.c_int64, _VP]),
+    "sa_cache_recache": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int32, _VP]),
+    "sa_window_attn_workspace": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+    "sa_window_attn": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _VP,
+                                      ctypes.c_size_t, _VP]),
+    "sa_cache_slots": (ctypes.c_int, [_VP, ctypes.POINTER(sa_slot), ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int32)]),
+    "sa_cache_read": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP, _VP]),
+    "sa_cache_counts": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
+    "sa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_version": (ctypes.c_char_p, []),
+}
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsinkattn.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sink_window_kv_amd.build` "
+                               "(there is no fallback implementation)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(status: int, fn: str):
+    if status != SA_OK:
+        raise SinkAttnError(status, fn, lib().sa_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_F32
+    raise SinkAttnError(SA_ERR_DTYPE, "dtype", f"unsupported tensor dtype {t.dtype}")
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes):
+    d = sa_rope_desc()
+    d.n_heads, d.head_dim = n_heads, head_dim
+    d.dim_t, d.dim_h, d.dim_w = dims
+    d.grid_h, d.grid_w = grid
+    d.theta0, d.sigma = float(theta0), float(sigma)
+    keep = None
+    if eps is not None:
+        keep = (ctypes.c_double * n_heads)(*[float(e) for e in eps])
+        d.eps = ctypes.cast(keep, ctypes.POINTER(ctypes.c_double))
+    d.jitter_axes = jitter_axes
+    return d, keep
+
+
+def sa_rope_tables(n_heads, head_dim, dims, grid, theta0=10000.0, sigma=0.0, eps=None,
+                   jitter_axes=SA_AXIS_T):
+    """Host-only tables: (theta_hat [H][3], freq [H][D/2]) as nested lists of floats."""
+    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes)
+    th = (ctypes.c_double * (n_heads * 3))()
+    fr = (ctypes.c_double * (n_heads * head_dim // 2))()
+    _check(lib().sa_rope_tables(ctypes.byref(d), th, fr), "sa_rope_tables")
+    return ([list(th[h * 3:(h + 1) * 3]) for h in range(n_heads)],
+            [list(fr[h * head_dim // 2:(h + 1) * head_dim // 2]) for h in range(n_heads)])
+
+
+class Rope:
+    """Owns an sa_rope handle (per-head fp64 frequency table on the device)."""
+
+    def __init__(self, n_heads, head_dim, dims, grid, theta0=10000.0, sigma=0.0, eps=None,
+                 jitter_axes=SA_AXIS_T):
+        self.n_heads, self.head_dim, self.dims, self.grid = n_heads, head_dim, tuple(dims), tuple(grid)
+        d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes)
+        h = _VP()
+        _check(lib().sa_rope_create(ctypes.byref(d), ctypes.byref(h)), "sa_rope_create")
+        self.handle = h
+
+    @property
+    def tokens_per_frame(self):
+        return self.grid[0] * self.grid[1]
+
+    def close(self):
+        if self.handle:
+            lib().sa_rope_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def sa_rope3d_apply(rope: Rope, x, y, batch: int, n_frames: int, t0: int, stream=None):
+    _check(lib().sa_rope3d_apply(rope.handle, _ptr(x), _ptr(y), _dtype_code(x), batch, n_frames, t0,
+                                 _stream(stream)), "sa_rope3d_apply")
+
+
+class Cache:
+    """Owns an sa_cache handle plus its two device stores (torch tensors)."""
+
+    def __init__(self, rope: Rope, batch: int, n_sink: int, n_local: int, dtype, device="cuda"):
+        import torch
+        code = SA_BF16 if dtype == torch.bfloat16 else SA_F32
+        d = sa_cache_desc()
+        d.batch, d.n_heads, d.head_dim = batch, rope.n_heads, rope.head_dim
+        d.tokens_per_frame, d.n_sink, d.n_local, d.dtype = rope.tokens_per_frame, n_sink, n_local, code
+        nbytes = lib().sa_cache_store_bytes(ctypes.byref(d))
+        if nbytes == 0:
+            raise SinkAttnError(SA_ERR_SHAPE, "sa_cache_store_bytes", "invalid cache descriptor")
+        elem = 2 if code == SA_BF16 else 4
+        self.k_store = torch.empty(nbytes // elem, dtype=dtype, device=device)
+        self.v_store = torch.empty(nbytes // elem, dtype=dtype, device=device)
+        d.k_store, d.v_store = self.k_store.data_ptr(), self.v_store.data_ptr()
+        h = _VP()
+        _check(lib().sa_cache_create(ctypes.byref(d), rope.handle, ctypes.byref(h)), "sa_cache_create")
+        self.handle = h
+        self.rope = rope
+        self.batch, self.n_sink, self.n_local, self.dtype = batch, n_sink, n_local, dtype
+
+    def close(self):
+        if self.handle:
+            lib().sa_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def sa_cache_reset(cache: Cache):
+    _check(lib().sa_cache_reset(cache.handle), "sa_cache_reset")
+
+
+def sa_cache_append(cache: Cache, k, v, n_frames: int, t0: int, stream=None):
+    _check(lib().sa_cache_append(cache.handle, _ptr(k), _ptr(v), n_frames, t0, _stream(stream)),
+           "sa_cache_append")
+
+
+def sa_cache_recache(cache: Cache, x, w_k, w_v, hidden: int, stream=None):
+    """w_k, w_v in the [H*D, hidden] (nn.Linear) layout."""
+    _check(lib().sa_cache_recache(cache.handle, _ptr(x), _ptr(w_k), _ptr(w_v), hidden, _stream(stream)),
+           "sa_cache_recache")
+
+
+def sa_window_attn_workspace(cache: Cache, n_q: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sa_window_attn_workspace(cache.handle, n_q, ctypes.byref(n)), "sa_window_attn_workspace")
+    return n.value
+
+
+def sa_window_attn(cache: Cache, q, o, n_q: int, scale: float = 0.0, mask: int = SA_MASK_NONE,
+                   workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sa_window_attn(cache.handle, _ptr(q), _ptr(o), n_q, scale, mask, _ptr(workspace),
+                                ws_bytes, _stream(stream)), "sa_window_attn")
+
+
+def sa_cache_slots(cache: Cache) -> List[sa_slot]:
+    n = ctypes.c_int32()
+    buf = (sa_slot * SA_MAX_FRAMES)()
+    _check(lib().sa_cache_slots(cache.handle, buf, SA_MAX_FRAMES, ctypes.byref(n)), "sa_cache_slots")
+    return [buf[i] for i in range(n.value)]
+
+
+def sa_cache_read(cache: Cache, index: int, k_out=None, v_out=None, stream=None):
+    _check(lib().sa_cache_read(cache.handle, index, _ptr(k_out), _ptr(v_out), _stream(stream)),
+           "sa_cache_read")
+
+
+def sa_cache_counts(cache: Cache):
+    a = ctypes.c_int64()
+    r = ctypes.c_int32()
+    _check(lib().sa_cache_counts(cache.handle, ctypes.byref(a), ctypes.byref(r)), "sa_cache_counts")
+    return a.value, r.value
+
+
+def sa_version() -> str:
+    return lib().sa_version().decode()

@@ -1,0 +1,391 @@
+// Host side of libsinkattn: handle management, validation, launch.
+//
+// Every entry point validates its arguments and the handle state before it
+// changes anything or launches; on error the handle is unchanged and the
+// thread-local last-error string says why.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/sinkattn.h"
+#include "cache_plan.hpp"
+#include "internal.hpp"
+#include "rope_tables.hpp"
+
+struct sa_rope {
+  int n_heads, head_dim;
+  int dims[3];
+  int grid_h, grid_w;
+  sa::RopeTables tables;
+  double* d_freq = nullptr;  // device [H][D/2]
+  int device = 0;
+};
+
+struct sa_cache {
+  sa_cache_desc desc;
+  const sa_rope* rope;
+  sa::CachePlan plan;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status fail(sa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+sa_status ok() {
+  g_last_error.clear();
+  return SA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(sa_dtype d) { return d == SA_BF16 ? 2 : 4; }
+
+sa_status hip_fail(hipError_t e, const char* what) {
+  return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+sa_status check_rope_desc(const sa_rope_desc* d) {
+  if (!d) return fail(SA_ERR_NULL, "rope descriptor is NULL");
+  if (d->n_heads < 1 || d->n_heads > 1024) return fail(SA_ERR_SHAPE, "n_heads must be in [1, 1024]");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(SA_ERR_SHAPE, "head_dim must be 64 or 128");
+  const int dims[3] = {d->dim_t, d->dim_h, d->dim_w};
+  for (int a = 0; a < 3; ++a)
+    if (dims[a] < 0 || dims[a] % 2) return fail(SA_ERR_SHAPE, "RoPE axis dims must be even and >= 0");
+  if (dims[0] + dims[1] + dims[2] != d->head_dim)
+    return fail(SA_ERR_SHAPE, "dim_t + dim_h + dim_w (%d) must equal head_dim (%d)",
+                dims[0] + dims[1] + dims[2], d->head_dim);
+  if (d->grid_h < 1 || d->grid_w < 1) return fail(SA_ERR_SHAPE, "grid must be >= 1x1");
+  const long long tf = static_cast<long long>(d->grid_h) * d->grid_w;
+  if (tf % 8 != 0 || tf > (1 << 20)) return fail(SA_ERR_SHAPE, "tokens per frame must be a multiple of 8 and <= 2^20");
+  if (!(d->theta0 > 1.0) || !std::isfinite(d->theta0)) return fail(SA_ERR_RANGE, "theta0 must be finite and > 1");
+  if (!(d->sigma >= 0.0) || !std::isfinite(d->sigma)) return fail(SA_ERR_RANGE, "sigma must be finite and >= 0");
+  if (d->jitter_axes > 7u) return fail(SA_ERR_RANGE, "jitter_axes must be a SA_AXIS_* mask");
+  if (d->eps) {
+    for (int h = 0; h < d->n_heads; ++h) {
+      const double e = d->eps[h];
+      if (!(e >= -1.0 && e <= 1.0)) return fail(SA_ERR_RANGE, "eps[%d] must be in [-1, 1]", h);
+      if (!(d->theta0 * (1.0 + d->sigma * e) > 1.0))
+        return fail(SA_ERR_RANGE, "jittered base of head %d is not > 1", h);
+    }
+  }
+  return SA_OK;
+}
+
+sa::RopeArgs rope_args(const sa_rope* r) {
+  sa::RopeArgs a;
+  a.freq = r->d_freq;
+  a.pairs_t = r->dims[0] / 2;
+  a.pairs_th = (r->dims[0] + r->dims[1]) / 2;
+  a.grid_w = r->grid_w;
+  return a;
+}
+
+sa::CacheGeom geom(const sa_cache* c) {
+  sa::CacheGeom g;
+  g.B = c->desc.batch;
+  g.H = c->desc.n_heads;
+  g.D = c->desc.head_dim;
+  g.T = c->desc.tokens_per_frame;
+  g.n_slots = c->desc.n_sink + c->desc.n_local;
+  g.k_store = c->desc.k_store;
+  g.v_store = c->desc.v_store;
+  return g;
+}
+
+sa::FrameTable resident_table(const sa_cache* c) {
+  sa::FrameTable ft{};
+  const auto res = c->plan.resident();
+  ft.n = static_cast<int32_t>(res.size());
+  for (size_t i = 0; i < res.size(); ++i) {
+    ft.store_slot[i] = res[i].store_slot;
+    ft.t[i] = res[i].t;
+  }
+  return ft;
+}
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_status_str(sa_status s) {
+  switch (s) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL: return "SA_ERR_NULL";
+    case SA_ERR_SHAPE: return "SA_ERR_SHAPE";
+    case SA_ERR_DTYPE: return "SA_ERR_DTYPE";
+    case SA_ERR_ALIGN: return "SA_ERR_ALIGN";
+    case SA_ERR_STATE: return "SA_ERR_STATE";
+    case SA_ERR_RANGE: return "SA_ERR_RANGE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+  }
+  return "SA_ERR_UNKNOWN";
+}
+
+const char* sa_last_error(void) { return g_last_error.c_str(); }
+
+const char* sa_version(void) { return "libsinkattn 0.1 (gfx950)"; }
+
+sa_status sa_rope_tables(const sa_rope_desc* desc, double* theta_hat_out, double* freq_out) {
+  if (sa_status s = check_rope_desc(desc)) return s;
+  const int dims[3] = {desc->dim_t, desc->dim_h, desc->dim_w};
+  const sa::RopeTables t = sa::build_rope_tables(desc->n_heads, desc->head_dim, dims, desc->theta0,
+                                                 desc->sigma, desc->eps, desc->jitter_axes);
+  if (theta_hat_out) std::memcpy(theta_hat_out, t.theta_hat.data(), t.theta_hat.size() * sizeof(double));
+  if (freq_out) std::memcpy(freq_out, t.freq.data(), t.freq.size() * sizeof(double));
+  return ok();
+}
+
+sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out) {
+  if (!out) return fail(SA_ERR_NULL, "out is NULL");
+  if (sa_status s = check_rope_desc(desc)) return s;
+  sa_rope* r = new (std::nothrow) sa_rope();
+  if (!r) return fail(SA_ERR_RANGE, "out of host memory");
+  r->n_heads = desc->n_heads;
+  r->head_dim = desc->head_dim;
+  r->dims[0] = desc->dim_t;
+  r->dims[1] = desc->dim_h;
+  r->dims[2] = desc->dim_w;
+  r->grid_h = desc->grid_h;
+  r->grid_w = desc->grid_w;
+  r->tables = sa::build_rope_tables(desc->n_heads, desc->head_dim, r->dims, desc->theta0,
+                                    desc->sigma, desc->eps, desc->jitter_axes);
+  hipError_t e = hipGetDevice(&r->device);
+  if (e == hipSuccess) e = hipMalloc(&r->d_freq, r->tables.freq.size() * sizeof(double));
+  if (e == hipSuccess)
+    e = hipMemcpy(r->d_freq, r->tables.freq.data(), r->tables.freq.size() * sizeof(double),
+                  hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (r->d_freq) (void)hipFree(r->d_freq);
+    delete r;
+    return hip_fail(e, "sa_rope_create");
+  }
+  *out = r;
+  return ok();
+}
+
+void sa_rope_destroy(sa_rope* r) {
+  if (!r) return;
+  if (r->d_freq) (void)hipFree(r->d_freq);
+  delete r;
+}
+
+sa_status sa_rope3d_apply(const sa_rope* rope, const void* x, void* y, sa_dtype dtype, int32_t batch,
+                          int32_t n_frames, int64_t t0, void* stream) {
+  if (!rope || !x || !y) return fail(SA_ERR_NULL, "rope, x and y must be non-NULL");
+  if (dtype != SA_BF16 && dtype != SA_F32) return fail(SA_ERR_DTYPE, "dtype must be SA_BF16 or SA_F32");
+  if (batch < 1 || n_frames < 1) return fail(SA_ERR_SHAPE, "batch and n_frames must be >= 1");
+  if (!aligned16(x) || !aligned16(y)) return fail(SA_ERR_ALIGN, "x and y must be 16-byte aligned");
+  if (t0 < 0 || t0 > (int64_t(1) << 40) - n_frames) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40)");
+  const int T = rope->grid_h * rope->grid_w;
+  const hipError_t e = sa::launch_rope3d(rope_args(rope), x, y, dtype, batch, rope->n_heads,
+                                         rope->head_dim, T, n_frames, t0,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope3d launch");
+  return ok();
+}
+
+size_t sa_cache_store_bytes(const sa_cache_desc* d) {
+  if (!d || d->batch < 1 || d->n_heads < 1 || (d->head_dim != 64 && d->head_dim != 128) ||
+      d->tokens_per_frame < 8 || d->n_sink < 0 || d->n_local < 1 ||
+      d->n_sink + d->n_local > SA_MAX_FRAMES || (d->dtype != SA_BF16 && d->dtype != SA_F32))
+    return 0;
+  return static_cast<size_t>(d->n_sink + d->n_local) * d->batch * d->n_heads * d->tokens_per_frame *
+         d->head_dim * elem_size(d->dtype);
+}
+
+sa_status sa_cache_create(const sa_cache_desc* d, const sa_rope* rope, sa_cache** out) {
+  if (!d || !rope || !out) return fail(SA_ERR_NULL, "desc, rope and out must be non-NULL");
+  if (!d->k_store || !d->v_store) return fail(SA_ERR_NULL, "k_store and v_store must be non-NULL");
+  if (d->dtype != SA_BF16 && d->dtype != SA_F32) return fail(SA_ERR_DTYPE, "dtype must be SA_BF16 or SA_F32");
+  if (d->batch < 1 || d->batch > 65535) return fail(SA_ERR_SHAPE, "batch must be in [1, 65535]");
+  if (d->n_sink < 0 || d->n_local < 1 || d->n_sink + d->n_local > SA_MAX_FRAMES)
+    return fail(SA_ERR_SHAPE, "need n_sink >= 0, n_local >= 1, n_sink + n_local <= %d", SA_MAX_FRAMES);
+  if (d->n_heads != rope->n_heads || d->head_dim != rope->head_dim)
+    return fail(SA_ERR_SHAPE, "cache heads/head_dim (%d, %d) differ from the rope's (%d, %d)", d->n_heads,
+                d->head_dim, rope->n_heads, rope->head_dim);
+  if (d->tokens_per_frame != rope->grid_h * rope->grid_w)
+    return fail(SA_ERR_SHAPE, "tokens_per_frame (%d) differs from the rope grid (%d x %d)", d->tokens_per_frame,
+                rope->grid_h, rope->grid_w);
+  if (!aligned16(d->k_store) || !aligned16(d->v_store)) return fail(SA_ERR_ALIGN, "stores must be 16-byte aligned");
+  // Every in-kernel index of one stream's queries and keys fits in int32.
+  const long long keys = static_cast<long long>(d->n_sink + d->n_local) * d->tokens_per_frame;
+  if (keys > (1LL << 30)) return fail(SA_ERR_SHAPE, "too many tokens in the window");
+  sa_cache* c = new (std::nothrow) sa_cache();
+  if (!c) return fail(SA_ERR_RANGE, "out of host memory");
+  c->desc = *d;
+  c->rope = rope;
+  c->plan = sa::CachePlan(d->n_sink, d->n_local);
+  *out = c;
+  return ok();
+}
+
+void sa_cache_destroy(sa_cache* c) { delete c; }
+
+sa_status sa_cache_reset(sa_cache* c) {
+  if (!c) return fail(SA_ERR_NULL, "cache is NULL");
+  c->plan.reset();
+  return ok();
+}
+
+sa_status sa_cache_append(sa_cache* c, const void* k, const void* v, int32_t n_frames, int64_t t0,
+                          void* stream) {
+  if (!c || !k || !v) return fail(SA_ERR_NULL, "cache, k and v must be non-NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(SA_ERR_ALIGN, "k and v must be 16-byte aligned");
+  if (t0 < 0 || t0 > (int64_t(1) << 40)) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40]");
+  switch (c->plan.check_append(n_frames, t0)) {
+    case 0: break;
+    case 1: return fail(SA_ERR_SHAPE, "n_frames must be in [1, %d]", SA_MAX_FRAMES);
+    case 2: return fail(SA_ERR_RANGE, "chunk of %d frames does not fit the %d-frame local window", n_frames,
+                        c->desc.n_local);
+    default: return fail(SA_ERR_RANGE, "t0 (%lld) must exceed the newest cached time (%lld)",
+                         static_cast<long long>(t0), static_cast<long long>(c->plan.newest_t()));
+  }
+  const auto planned = c->plan.plan_append(n_frames, t0);
+  sa::FrameTable chunk{};
+  chunk.n = n_frames;
+  for (int i = 0; i < n_frames; ++i) {
+    chunk.store_slot[i] = planned[i].store_slot;
+    chunk.t[i] = planned[i].t;
+  }
+  const hipError_t e = sa::launch_append(rope_args(c->rope), geom(c), k, v, c->desc.dtype, chunk,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  c->plan.commit_append(n_frames, t0);
+  return ok();
+}
+
+sa_status sa_cache_recache(sa_cache* c, const void* x, const void* w_k, const void* w_v, int32_t hidden,
+                           void* stream) {
+  if (!c || !x || !w_k || !w_v) return fail(SA_ERR_NULL, "cache, x, w_k and w_v must be non-NULL");
+  if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v)) return fail(SA_ERR_ALIGN, "x and weights must be 16-byte aligned");
+  if (hidden < 64 || hidden % 64 != 0 || hidden > (1 << 16))
+    return fail(SA_ERR_SHAPE, "hidden must be a multiple of 64 in [64, 65536]");
+  if ((2 * c->desc.n_heads * c->desc.head_dim) % 128 != 0)
+    return fail(SA_ERR_SHAPE, "2 * n_heads * head_dim must be a multiple of 128");
+  if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "recache on an empty cache");
+  sa::RecacheArgs a;
+  a.x = x;
+  a.wk = w_k;
+  a.wv = w_v;
+  a.hidden = hidden;
+  a.g = geom(c);
+  a.rope = rope_args(c->rope);
+  a.frames = resident_table(c);
+  const hipError_t e = sa::launch_recache(a, c->desc.dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "recache launch");
+  return ok();
+}
+
+static sa_status attn_plan(const sa_cache* c, int32_t n_q, int* splits, size_t* bytes) {
+  if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "attention on an empty cache");
+  const auto res = c->plan.resident();
+  if (n_q < 1 || n_q > static_cast<int32_t>(res.size()))
+    return fail(SA_ERR_SHAPE, "n_q (%d) must be in [1, resident frames = %d]", n_q, static_cast<int>(res.size()));
+  // The query frames are the newest n_q appended frames; they must all still be resident.
+  if (res.back().frame - (n_q - 1) != res[res.size() - n_q].frame)
+    return fail(SA_ERR_RANGE, "the newest %d frames are not all resident", n_q);
+  const long long lq = static_cast<long long>(n_q) * c->desc.tokens_per_frame;
+  if (lq * c->desc.batch > (1LL << 31) / 4) return fail(SA_ERR_SHAPE, "query chunk too large");
+  const int s = sa::attn_num_splits(c->desc.dtype, c->desc.batch, c->desc.n_heads, c->desc.head_dim,
+                                    c->desc.tokens_per_frame, n_q, static_cast<int>(res.size()), device_cus());
+  *splits = s;
+  *bytes = sa::attn_workspace_bytes(c->desc.dtype, c->desc.batch, c->desc.n_heads, c->desc.head_dim,
+                                    c->desc.tokens_per_frame, n_q, s);
+  return SA_OK;
+}
+
+sa_status sa_window_attn_workspace(const sa_cache* c, int32_t n_q, size_t* bytes) {
+  if (!c || !bytes) return fail(SA_ERR_NULL, "cache and bytes must be non-NULL");
+  int splits = 1;
+  if (sa_status s = attn_plan(c, n_q, &splits, bytes)) return s;
+  return ok();
+}
+
+sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q, float scale, sa_mask mask,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!c || !q || !o) return fail(SA_ERR_NULL, "cache, q and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(o) || !aligned16(workspace)) return fail(SA_ERR_ALIGN, "q, o and workspace must be 16-byte aligned");
+  if (q == o) return fail(SA_ERR_RANGE, "o must not alias q");
+  if (mask != SA_MASK_NONE && mask != SA_MASK_FRAME_CAUSAL) return fail(SA_ERR_RANGE, "unknown mask");
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return fail(SA_ERR_RANGE, "scale must be finite and >= 0");
+  int splits = 1;
+  size_t need = 0;
+  if (sa_status s = attn_plan(c, n_q, &splits, &need)) return s;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SA_ERR_RANGE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  sa::AttnArgs a;
+  a.q = q;
+  a.o = o;
+  a.g = geom(c);
+  a.rope = rope_args(c->rope);
+  a.frames = resident_table(c);
+  a.n_q = n_q;
+  a.causal = mask == SA_MASK_FRAME_CAUSAL ? 1 : 0;
+  const float sc = scale == 0.f ? 1.f / std::sqrt(static_cast<float>(c->desc.head_dim)) : scale;
+  a.scale_log2 = static_cast<float>(static_cast<double>(sc) * 1.4426950408889634);
+  a.n_splits = splits;
+  a.ws = static_cast<float*>(workspace);
+  const hipError_t e = sa::launch_window_attn(a, c->desc.dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+sa_status sa_cache_slots(const sa_cache* c, sa_slot* out, int32_t cap, int32_t* n_valid) {
+  if (!c || !n_valid) return fail(SA_ERR_NULL, "cache and n_valid must be non-NULL");
+  if (cap > 0 && !out) return fail(SA_ERR_NULL, "out is NULL with cap > 0");
+  const auto res = c->plan.resident();
+  *n_valid = static_cast<int32_t>(res.size());
+  for (int32_t i = 0; i < cap && i < static_cast<int32_t>(res.size()); ++i) {
+    out[i].frame = res[i].frame;
+    out[i].t = res[i].t;
+    out[i].segment = res[i].segment;
+    out[i].slot = res[i].slot;
+  }
+  return ok();
+}
+
+sa_status sa_cache_read(const sa_cache* c, int32_t index, void* k_out, void* v_out, void* stream) {
+  if (!c) return fail(SA_ERR_NULL, "cache is NULL");
+  if (!k_out && !v_out) return fail(SA_ERR_NULL, "k_out and v_out are both NULL");
+  const auto res = c->plan.resident();
+  if (index < 0 || index >= static_cast<int32_t>(res.size()))
+    return fail(SA_ERR_RANGE, "index %d outside the %d resident frames", index, static_cast<int>(res.size()));
+  const hipError_t e = sa::launch_read(geom(c), res[index].store_slot, k_out, v_out, c->desc.dtype,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read launch");
+  return ok();
+}
+
+sa_status sa_cache_counts(const sa_cache* c, int64_t* n_appended, int32_t* n_resident) {
+  if (!c) return fail(SA_ERR_NULL, "cache is NULL");
+  if (n_appended) *n_appended = c->plan.n_appended();
+  if (n_resident) *n_resident = static_cast<int32_t>(c->plan.resident().size());
+  return ok();
+}
+
+}  // extern "C"

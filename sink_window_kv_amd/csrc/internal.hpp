@@ -1,0 +1,77 @@
+// Internal interface between the host API (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "cache_plan.hpp"
+
+namespace sa {
+
+enum ElemType : int { kBF16 = 0, kF32 = 1 };
+
+// Device view of a RoPE handle.
+struct RopeArgs {
+  const double* freq;  // device [H][D/2], fp64
+  int32_t pairs_t;     // pairs [0, pairs_t) rotate with the time position
+  int32_t pairs_th;    // pairs [pairs_t, pairs_th) with the grid row, the rest with the column
+  int32_t grid_w;
+};
+
+// Per-call table of frames, passed by value as a kernel argument.
+struct FrameTable {
+  int32_t n;
+  int32_t store_slot[kMaxFrames];
+  int64_t t[kMaxFrames];
+};
+
+// Cache geometry and stores.
+struct CacheGeom {
+  int32_t B, H, D, T;  // streams, heads, head size, tokens per frame
+  int32_t n_slots;     // n_sink + n_local
+  void* k_store;       // [n_slots][B][H][T][D]
+  void* v_store;       // [n_slots][B][H][D][T]
+};
+
+struct AttnArgs {
+  const void* q;  // [B, n_q*T, H, D]
+  void* o;        // [B, n_q*T, H, D]
+  CacheGeom g;
+  RopeArgs rope;
+  FrameTable frames;  // resident frames, logical order; the queries are the last n_q
+  int32_t n_q;
+  int32_t causal;
+  float scale_log2;   // softmax scale * log2(e)
+  int32_t n_splits;   // key splits (1 = no workspace)
+  float* ws;          // split partials, see attn_workspace_bytes
+};
+
+struct RecacheArgs {
+  const void* x;   // [B, n_res*T, C]
+  const void* wk;  // [H*D, C]
+  const void* wv;  // [H*D, C]
+  int32_t hidden;  // C
+  CacheGeom g;
+  RopeArgs rope;
+  FrameTable frames;  // resident frames, logical order
+};
+
+hipError_t launch_rope3d(const RopeArgs& rope, const void* x, void* y, int dtype, int B, int H,
+                         int D, int T, int n_frames, int64_t t0, hipStream_t stream);
+
+hipError_t launch_append(const RopeArgs& rope, const CacheGeom& g, const void* k, const void* v,
+                         int dtype, const FrameTable& chunk, hipStream_t stream);
+
+hipError_t launch_read(const CacheGeom& g, int store_slot, void* k_out, void* v_out, int dtype,
+                       hipStream_t stream);
+
+// Number of key splits the attention launch uses for this shape.
+int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus);
+size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits);
+hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream);
+
+hipError_t launch_recache(const RecacheArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,537 @@
+// Sink + short-window attention over the frame cache.
+//
+// Computes, per stream b and head h, o = softmax(RoPE(q) K^T * scale) V over
+// the resident frames (LongLive paper review, section 3 "Short-Window
+// Attention" equation with the pinned frames of "Frame Sink"; LoL paper
+// review, background "multi-head attention" equation).  Queries are the
+// newest n_q resident frames; with the frame-causal mask a query of frame f
+// sees the resident frames up to f.  Because resident frames are kept in
+// increasing frame order, every query row sees a prefix [0, kend) of the
+// logical key sequence.
+//
+// bf16 kernel (gfx950 matrix cores), per workgroup of 4 waves:
+//   * each wave owns 32 query rows; the wave computes S^T = K Q^T with
+//     v_mfma_f32_32x32x16_bf16 so that every lane holds the scores of ONE
+//     query (column) for 16 keys per 32-key block -- the row max and row sum
+//     are in-lane plus one exchange between the two half-waves;
+//   * the keys of each 32-key block are permuted (bits 2 and 3 of the row
+//     index swapped) when the K operand is read from LDS, so that the score
+//     registers are already in the order the P^T operand of the second
+//     product needs: O^T += V^T P^T runs straight from registers;
+//   * V is stored transposed in the cache ([D][T] per slot, stream, head), so
+//     the V^T operand is a plain 16-byte LDS read;
+//   * q is rotated (RoPE) in fp32 as it is loaded, then rounded to bf16;
+//   * online softmax in the exp2 domain, fp32 statistics;
+//   * K and V^T tiles of 64 keys are staged in LDS; per-key addresses come
+//     from the per-frame slot table, so sink and ring frames are read in
+//     place with no gather copy.
+// For one stream at Wan-1.3B shapes the (q-tile, head) grid alone does not
+// fill 256 CUs, so the key range is split; each split publishes a partial
+// (O, m, l) and the last split of a q-tile to arrive (atomic counter) merges
+// them in split order (deterministic) -- one kernel per call.
+//
+// fp32 kernel: one thread per query row, VALU FMA, for the small fp32
+// configurations (accuracy 1e-5 against an fp64 reference).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+
+#include "device_common.hpp"
+
+namespace sa {
+namespace {
+
+typedef __bf16 mfma_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float mfma_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int kWaves = 4;
+constexpr int kQW = 32;                 // query rows per wave
+constexpr int kQTile = kWaves * kQW;    // query rows per workgroup
+constexpr int kKTile = 64;              // keys per iteration
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ int key_perm(int m) {  // swap bits 2 and 3
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(mfma_bf16x8, v);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16x2 with the hardware converter (round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Workspace layout (float units): [0, 1024) int32 arrival counters, one per
+// (stream, head, q-tile); then split partials O [S][B][H][Lq][D] (fp32,
+// unnormalised) and (m, l) [S][B][H][Lq][2].  The counters must be zero
+// before the first call; the last-arriving workgroup of a tile resets its
+// counter, so every call leaves them zero again.
+constexpr int kMaxTileCounters = 1024;
+
+template <int D>
+struct AttnSmem {
+  uint16_t k[2][kKTile][D + 8];   // keys x channels (+16 B pad), double-buffered
+  uint16_t vt[2][D][kKTile + 8];  // channels x keys (+16 B pad)
+};
+
+// Map the hardware workgroup id to a logical one so that each XCD (workgroups
+// are dealt round-robin to the 8 XCDs) gets a contiguous range of logical
+// ids: the q-tiles of one (stream, head, split) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  constexpr int X = 8;
+  const int xcd = pid % X;
+  const int local = pid / X;
+  const int per = (n + X - 1) / X;
+  const int tall = n % X == 0 ? X : n % X;
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
+  __shared__ AttnSmem<D> sm;
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const CacheGeom& g = a.g;
+  const int T = g.T;
+  const int Lq = a.n_q * T;
+  const int n_qt = (Lq + kQTile - 1) / kQTile;
+  // logical id = ((b*H + h) * S + split) * n_qt + qt
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = lid % n_qt;
+  const int split = (lid / n_qt) % a.n_splits;
+  const int bh = lid / (n_qt * a.n_splits);
+  const int b = bh / g.H;
+  const int h = bh - b * g.H;
+  const int n_res = a.frames.n;
+  const int first_q = n_res - a.n_q;  // logical index of the first query frame
+  const int row = qt * kQTile + wave * kQW + n;
+  const bool row_ok = row < Lq;
+  const int qf = row_ok ? row / T : a.n_q - 1;
+  const int n_keys = n_res * T;
+  const int kend = a.causal ? (first_q + qf + 1) * T : n_keys;
+  // Rows of this wave / workgroup (wave-uniform and block-uniform bounds).
+  const int wave_row0 = qt * kQTile + wave * kQW;
+  const bool wave_active = wave_row0 < Lq;
+  const int wave_last = min(wave_row0 + kQW - 1, Lq - 1);
+  const int wave_kend = a.causal ? (first_q + wave_last / T + 1) * T : n_keys;
+  const int last_row = min(qt * kQTile + kQTile - 1, Lq - 1);
+  const int kend_wg = a.causal ? (first_q + last_row / T + 1) * T : n_keys;
+  const int n_tiles = (kend_wg + kKTile - 1) / kKTile;
+  const int tile_lo = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / a.n_splits);
+  const int tile_hi = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / a.n_splits);
+
+  // ---- Q fragment: rotate in fp32, round to bf16 (B operand of S^T = K Q^T).
+  mfma_bf16x8 qfrag[D / 16];
+  {
+    const double* freq_h = a.rope.freq + static_cast<size_t>(h) * (D / 2);
+    const int tok = row_ok ? row - qf * T : 0;
+    const int64_t t = a.frames.t[first_q + qf];
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) {
+        float x[8];
+        unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
+        rope_rotate8(a.rope, freq_h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+        v = pack_bf16x8(x);
+      }
+      qfrag[s] = as_bf16x8(v);
+    }
+  }
+
+  mfma_f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = kNegInf;  // running max of scaled (log2-domain) scores
+  float l_run = 0.f;      // this half-wave's partial row sum
+
+  const uint16_t* kst = static_cast<const uint16_t*>(g.k_store);
+  const uint16_t* vst = static_cast<const uint16_t*>(g.v_store);
+  const int64_t head_off = static_cast<int64_t>(b) * g.H + h;  // within a slot
+  const int64_t slot_stride = static_cast<int64_t>(g.B) * g.H;
+
+  // Each thread moves 4 K vectors and 4 V^T vectors (16 B) per tile.
+  constexpr int KV = D / 8;                            // vectors per key row
+  constexpr int KVEC = kKTile * KV / 256;              // K vectors per thread
+  constexpr int VVEC = D * (kKTile / 8) / 256;         // V^T vectors per thread
+  u32x4 kreg[KVEC], vreg[VVEC];
+  auto load_tile = [&](int kt) {
+    const int j0 = kt * kKTile;
+#pragma unroll
+    for (int u = 0; u < KVEC; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      const int r = e / KV, c = e % KV;
+      const int j = j0 + r;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j < kend_wg) {
+        const int lf = j / T;
+        const int tok = j - lf * T;
+        v = *reinterpret_cast<const u32x4*>(
+            kst + ((a.frames.store_slot[lf] * slot_stride + head_off) * T + tok) * static_cast<int64_t>(D) + c * 8);
+      }
+      kreg[u] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < VVEC; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      const int d = e / (kKTile / 8), c = e % (kKTile / 8);
+      const int j = j0 + c * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j < kend_wg) {
+        const int lf = j / T;
+        const int tok = j - lf * T;
+        v = *reinterpret_cast<const u32x4*>(
+            vst + ((a.frames.store_slot[lf] * slot_stride + head_off) * D + d) * static_cast<int64_t>(T) + tok);
+      }
+      vreg[u] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KVEC; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      *reinterpret_cast<u32x4*>(&sm.k[buf][e / KV][(e % KV) * 8]) = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VVEC; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      *reinterpret_cast<u32x4*>(&sm.vt[buf][e / (kKTile / 8)][(e % (kKTile / 8)) * 8]) = vreg[u];
+    }
+  };
+
+  if (tile_lo < tile_hi) {
+    load_tile(tile_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int kt = tile_lo; kt < tile_hi; ++kt) {
+    const int buf = (kt - tile_lo) & 1;
+    const int j0 = kt * kKTile;
+    if (kt + 1 < tile_hi) load_tile(kt + 1);  // in flight during this tile's math
+
+    if (wave_active && j0 < wave_kend) {
+      // ---- S^T = K Q^T for two 32-key blocks.
+      mfma_f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+        const int krow = kb * 32 + key_perm(n);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const mfma_bf16x8 kf =
+              as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][krow][16 * s + 8 * hh]));
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qfrag[s], sacc[kb], 0, 0, 0);
+        }
+      }
+
+      // ---- mask (register i of block kb holds key j0 + 32kb + 16(i/8) + 8hh + i%8)
+      if (j0 + kKTile > kend) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j0 + kb * 32 + 16 * (i >> 3) + 8 * hh + (i & 7);
+            if (key >= kend) sacc[kb][i] = kNegInf;
+          }
+      }
+
+      // ---- online softmax (log2 domain), per lane = per query.
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+      u32x4 pk[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], a.scale_log2, -m_use));
+          psum += p[i];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pk[kb][s2][w] = cvt_pk_bf16(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const mfma_bf16x8 vf = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(&sm.vt[buf][32 * db + n][kb * 32 + 16 * s2 + 8 * hh]));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pk[kb][s2]), oacc[db],
+                                                               0, 0, 0);
+          }
+      }
+    }
+    if (kt + 1 < tile_hi) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds O^T[d][row] for d = 32db + 8(i/4) + 4hh + i%4.
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (a.n_splits > 1) {
+    // Publish this split's partial, then the last-arriving split of the
+    // q-tile merges all of them (fixed split order, so results are
+    // deterministic) and writes O.
+    const int64_t plane = static_cast<int64_t>(g.B) * g.H * Lq;
+    float* part_o = a.ws + kMaxTileCounters;
+    float* part_ml = part_o + static_cast<int64_t>(a.n_splits) * plane * D;
+    const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
+    if (row_ok) {
+      float* po = part_o + (split * plane + prow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 w = {oacc[db][4 * gq], oacc[db][4 * gq + 1], oacc[db][4 * gq + 2], oacc[db][4 * gq + 3]};
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
+        }
+      if (hh == 0) {
+        part_ml[(split * plane + prow) * 2] = m_run;
+        part_ml[(split * plane + prow) * 2 + 1] = l_tot;
+      }
+    }
+    __threadfence();
+    __syncthreads();
+    int* counters = reinterpret_cast<int*>(a.ws);
+    const int tile_id = bh * n_qt + qt;
+    if (threadIdx.x == 0) {
+      const int prev = atomicAdd(&counters[tile_id], 1);
+      s_last = prev == a.n_splits - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (threadIdx.x == 0) atomicExch(&counters[tile_id], 0);
+    if (!row_ok) return;
+    float M = kNegInf;
+    for (int s = 0; s < a.n_splits; ++s) {
+      const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
+      M = fmaxf(M, ms);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    l_tot = 0.f;
+    for (int s = 0; s < a.n_splits; ++s) {
+      const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
+      if (ms == kNegInf) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - M);
+      l_tot += __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2 + 1]) * w;
+      const float* po = part_o + (s * plane + prow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 32 * db + 8 * gq + 4 * hh));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[db][4 * gq + i] += x[i] * w;
+        }
+    }
+  }
+  if (row_ok) {
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint2 w;
+        w.x = cvt_pk_bf16(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
+        w.y = cvt_pk_bf16(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * hh) = w;
+      }
+  }
+}
+
+// fp32 path: one thread per query row, 32-key tiles staged in LDS.
+constexpr int kF32Rows = 64;
+constexpr int kF32Keys = 32;
+
+template <int D>
+__global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
+  __shared__ float ks[kF32Keys][D + 1];
+  __shared__ float vs[kF32Keys][D + 1];
+  const CacheGeom& g = a.g;
+  const int T = g.T;
+  const int b = blockIdx.y / g.H;
+  const int h = blockIdx.y - b * g.H;
+  const int Lq = a.n_q * T;
+  const int n_res = a.frames.n;
+  const int first_q = n_res - a.n_q;
+  const int row = blockIdx.x * kF32Rows + threadIdx.x;
+  const bool row_ok = row < Lq;
+  const int qf = row_ok ? row / T : a.n_q - 1;
+  const int n_keys = n_res * T;
+  const int kend = a.causal ? (first_q + qf + 1) * T : n_keys;
+  const int last_row = min(static_cast<int>(blockIdx.x) * kF32Rows + kF32Rows - 1, Lq - 1);
+  const int kend_wg = a.causal ? (first_q + last_row / T + 1) * T : n_keys;
+
+  float q[D];
+  {
+    const int tok = row_ok ? row - qf * T : 0;
+    const int64_t t = a.frames.t[first_q + qf];
+    const float* qrow = static_cast<const float*>(a.q) + ((static_cast<int64_t>(b) * Lq + (row_ok ? row : 0)) * g.H + h) * D;
+    const double* freq_h = a.rope.freq + static_cast<size_t>(h) * (D / 2);
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = row_ok ? qrow[c * 8 + i] : 0.f;
+      rope_rotate8(a.rope, freq_h, c, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[c * 8 + i] = x[i];
+    }
+  }
+  float o[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) o[d] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+  const float* kst = static_cast<const float*>(g.k_store);
+  const float* vst = static_cast<const float*>(g.v_store);
+  const int64_t head_off = static_cast<int64_t>(b) * g.H + h;
+
+  for (int j0 = 0; j0 < kend_wg; j0 += kF32Keys) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kF32Keys * D; e += kF32Rows) {
+      const int r = e / D, d = e - (e / D) * D;
+      const int j = j0 + r;
+      float kv = 0.f, vv = 0.f;
+      if (j < kend_wg) {
+        const int lf = j / T;
+        const int tok = j - lf * T;
+        const int64_t base = static_cast<int64_t>(a.frames.store_slot[lf]) * g.B * g.H + head_off;
+        kv = kst[(base * T + tok) * D + d];
+        vv = vst[(base * D + d) * static_cast<int64_t>(T) + tok];
+      }
+      ks[r][d] = kv;
+      vs[r][d] = vv;
+    }
+    __syncthreads();
+    float s[kF32Keys];
+    float mx = kNegInf;
+#pragma unroll 4
+    for (int r = 0; r < kF32Keys; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc = fmaf(q[d], ks[r][d], acc);
+      s[r] = (j0 + r < kend) ? acc * a.scale_log2 : kNegInf;
+      mx = fmaxf(mx, s[r]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] *= alpha;
+    for (int r = 0; r < kF32Keys; ++r) {
+      const float p = exp2f(s[r] - m_use);
+      l_run += p;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] = fmaf(p, vs[r][d], o[d]);
+    }
+  }
+  if (row_ok) {
+    const float inv = 1.f / l_run;
+    float* orow = static_cast<float*>(a.o) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) orow[d] = o[d] * inv;
+  }
+}
+
+}  // namespace
+
+int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus) {
+  (void)D;
+  if (dtype != kBF16) return 1;
+  const int64_t tiles = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + kQTile - 1) / kQTile);
+  const int64_t key_tiles = (static_cast<int64_t>(n_res) * T + kKTile - 1) / kKTile;
+  if (tiles > kMaxTileCounters) return 1;
+  int64_t max_s = key_tiles / 8;  // at least 8 key tiles per split
+  if (max_s > 16) max_s = 16;
+  if (max_s < 1) max_s = 1;
+  if (const char* env = std::getenv("SA_ATTN_SPLITS")) {
+    const int v = std::atoi(env);
+    if (v >= 1) return static_cast<int>(v < max_s ? v : max_s);
+  }
+  // Two workgroups fit a CU.  Pick the split count whose workgroup count
+  // best fills whole rounds of 2 x CUs, with a small charge per split for
+  // the partial results it writes and merges.
+  const double slots = 2.0 * num_cus;
+  int best = 1;
+  double best_score = -1.0;
+  for (int64_t s = 1; s <= max_s; ++s) {
+    const double wgs = static_cast<double>(tiles * s);
+    const double rounds = std::ceil(wgs / slots);
+    const double score = wgs / (rounds * slots) - (s > 1 ? 0.01 * s : 0.0);
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = static_cast<int>(s);
+    }
+  }
+  return best;
+}
+
+size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits) {
+  if (dtype != kBF16 || n_splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * H * n_q * T;
+  return (static_cast<size_t>(kMaxTileCounters) + static_cast<size_t>(n_splits) * rows * (D + 2)) * sizeof(float);
+}
+
+hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) {
+  const int Lq = a.n_q * a.g.T;
+  const int BH = a.g.B * a.g.H;
+  if (dtype == kBF16) {
+    const int64_t wgs = static_cast<int64_t>((Lq + kQTile - 1) / kQTile) * BH * a.n_splits;
+    const dim3 grid(static_cast<unsigned>(wgs));
+    if (a.g.D == 128)
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
+  } else {
+    const dim3 grid((Lq + kF32Rows - 1) / kF32Rows, BH, 1);
+    if (a.g.D == 128)
+      hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(kF32Rows), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(kF32Rows), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,124 @@
+"""CPU tests of the host side: exported C-ABI symbols, host RoPE tables,
+argument validation that needs no device, and the cache plan (g++ harness)
+against the oracle's cache model."""
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from oracle import cache as ocache
+from oracle import rope as orope
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+
+
+def _swk():
+    import sink_window_kv_amd as swk
+    if not os.path.exists(swk.LIB_PATH):
+        from sink_window_kv_amd import build
+        build.build()
+    return swk
+
+
+def test_library_exports_every_declared_symbol():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", src)))
+    assert len(names) >= 18
+    lib = _swk().lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"symbols declared but not exported: {missing}"
+    assert _swk().sa_version().startswith("libsinkattn")
+
+
+@pytest.mark.parametrize("sigma,axes,names", [(0.0, 1, ("t",)), (0.8, 1, ("t",)), (0.8, 7, ("t", "h", "w")),
+                                              (0.3, 6, ("h", "w"))])
+def test_host_rope_tables_match_oracle(sigma, axes, names):
+    swk = _swk()
+    eps = np.random.default_rng(3).uniform(-1, 1, 12)
+    th, fr = swk.sa_rope_tables(12, 128, (44, 42, 42), (30, 52), 10000.0, sigma, eps, axes)
+    bases = orope.theta_hat(10000.0, sigma, eps, jitter_axes=names)
+    np.testing.assert_allclose(np.array(th), bases, rtol=1e-15)
+    for h in range(12):
+        np.testing.assert_allclose(fr[h], orope.head_frequencies(bases[h], (44, 42, 42)), rtol=1e-14)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2), (dict(dims=(44, 42, 40)), 2), (dict(dims=(43, 43, 42)), 2),
+    (dict(grid=(3, 3)), 2), (dict(theta0=1.0), 6), (dict(sigma=-0.1), 6),
+    (dict(eps=[1.5] * 12), 6), (dict(sigma=1.0, eps=[-1.0] * 12), 6), (dict(jitter_axes=8), 6),
+])
+def test_host_rope_validation(kw, status):
+    swk = _swk()
+    args = dict(n_heads=12, head_dim=128, dims=(44, 42, 42), grid=(30, 52), theta0=10000.0, sigma=0.8,
+                eps=[0.0] * 12, jitter_axes=1)
+    args.update(kw)
+    with pytest.raises(swk.SinkAttnError) as e:
+        swk.sa_rope_tables(**args)
+    assert e.value.status == status
+    assert swk.lib().sa_last_error().decode() != ""
+
+
+def test_host_cache_store_bytes_and_null_checks():
+    import ctypes
+    swk = _swk()
+    d = swk.sa_cache_desc()
+    d.batch, d.n_heads, d.head_dim, d.tokens_per_frame, d.n_sink, d.n_local, d.dtype = 1, 12, 128, 1560, 3, 9, 0
+    assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 12 * 12 * 1560 * 128 * 2
+    d.dtype = 1
+    assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 12 * 12 * 1560 * 128 * 4
+    d.n_local = 0
+    assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 0
+    d.n_local, d.n_sink = 60, 5
+    assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 0
+    h = ctypes.c_void_p()
+    assert swk.lib().sa_cache_create(None, None, ctypes.byref(h)) == swk.SA_ERR_NULL
+    assert swk.lib().sa_window_attn(None, None, None, 1, 0.0, 0, None, 0, None) == swk.SA_ERR_NULL
+    assert swk.lib().sa_cache_append(None, None, None, 1, 0, None) == swk.SA_ERR_NULL
+    assert swk.lib().sa_status_str(6) == b"SA_ERR_RANGE"
+
+
+@pytest.fixture(scope="module")
+def plan_harness():
+    exe = os.path.join(tempfile.mkdtemp(prefix="swk_plan_"), "plan_harness")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror",
+                    "-I", os.path.join(ROOT, "sink_window_kv_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "cpp", "plan_harness.cpp"), "-o", exe], check=True)
+    return exe
+
+
+def _run_plan(exe, n_sink, n_local, cmds):
+    inp = f"{n_sink} {n_local}\n" + "\n".join(cmds) + "\n"
+    out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+    rows = []
+    for line in out.strip().splitlines():
+        parts = line.split()
+        ents = [tuple(int(x) for x in p.split(",")) for p in parts[2:]]
+        rows.append((int(parts[0]), int(parts[1]), ents))
+    return rows
+
+
+@pytest.mark.parametrize("n_sink,n_local,chunk", [(1, 2, 1), (3, 9, 1), (3, 9, 3), (0, 5, 2), (2, 4, 3), (0, 64, 7)])
+def test_cache_plan_matches_oracle_model(plan_harness, n_sink, n_local, chunk):
+    cmds, t0s = [], []
+    t = 0
+    for f0 in range(0, 40, chunk):
+        cmds.append(f"a {chunk} {t}")
+        t0s.append(t)
+        t += chunk + (f0 % 3)  # gaps between chunks are allowed; consecutive inside a chunk
+    rows = _run_plan(plan_harness, n_sink, n_local, cmds)
+    m = ocache.CacheModel(n_sink, n_local)
+    for (code, n_app, ents), t0 in zip(rows, t0s):
+        m.append(chunk, t0)
+        assert code == 0 and n_app == m.n_appended
+        assert ents == [(e.frame, e.t, e.segment, e.slot) for e in m.slots()]
+
+
+def test_cache_plan_rejections_and_reset(plan_harness):
+    rows = _run_plan(plan_harness, 3, 9, ["a 3 0", "a 10 3", "a 1 2", "a 0 9", "a 9 3", "r", "a 1 0"])
+    assert [r[0] for r in rows] == [0, 2, 3, 1, 0, 0, 0]
+    assert rows[4][1] == 12 and rows[5][1] == 0 and rows[6][2] == [(0, 0, 0, 0)]
