@@ -46,10 +46,14 @@ typedef __bf16 mfma_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float mfma_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int kWaves = 4;
-constexpr int kQW = 32;                 // query rows per wave
+constexpr int kQB = 2;                  // 32-row query blocks per wave
+constexpr int kQW = 32 * kQB;           // query rows per wave
 constexpr int kQTile = kWaves * kQW;    // query rows per workgroup
 constexpr int kKTile = 64;              // keys per iteration
 constexpr float kNegInf = -__builtin_huge_valf();
+// Lazy rescaling: the running max used for exp2 is only raised when a new
+// score exceeds it by more than this (log2 units), so p <= 2^kLazy.
+constexpr float kLazy = 8.f;
 
 __device__ __forceinline__ int key_perm(int m) {  // swap bits 2 and 3
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -75,10 +79,20 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // counter, so every call leaves them zero again.
 constexpr int kMaxTileCounters = 1024;
 
+// LDS tile layout (16-byte chunks, no padding, XOR-swizzled so that the 16
+// lanes of a matrix-core operand read hit 16 distinct bank groups):
+//   K   : 64 keys x (D/8) chunks, chunk (r, c) at r*(D/8) + (c ^ kswz(r))
+//   V^T : D rows x 8 chunks (8 keys each), chunk (d, c) at d*8 + (c ^ vswz(d))
 template <int D>
-struct AttnSmem {
-  uint16_t k[2][kKTile][D + 8];   // keys x channels (+16 B pad), double-buffered
-  uint16_t vt[2][D][kKTile + 8];  // channels x keys (+16 B pad)
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+template <int D>
+struct TileSmem {
+  u32x4 k[kKTile * D / 8];
+  u32x4 vt[D * kKTile / 8];
 };
 
 // Map the hardware workgroup id to a logical one so that each XCD (workgroups
@@ -93,9 +107,12 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
-template <int D>
-__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
-  __shared__ AttnSmem<D> sm;
+// BIG_T: every 64-key tile spans at most two frames (T >= 64), so frame and
+// slot are resolved once per tile with scalar arithmetic.
+template <int D, bool BIG_T>
+__global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
+  __shared__ TileSmem<D> sm[2];
+  __shared__ int s_slot[kMaxFrames];
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -114,12 +131,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   const int h = bh - b * g.H;
   const int n_res = a.frames.n;
   const int first_q = n_res - a.n_q;  // logical index of the first query frame
-  const int row = qt * kQTile + wave * kQW + n;
-  const bool row_ok = row < Lq;
-  const int qf = row_ok ? row / T : a.n_q - 1;
   const int n_keys = n_res * T;
-  const int kend = a.causal ? (first_q + qf + 1) * T : n_keys;
-  // Rows of this wave / workgroup (wave-uniform and block-uniform bounds).
+  if (threadIdx.x < kMaxFrames) s_slot[threadIdx.x] = threadIdx.x < n_res ? a.frames.store_slot[threadIdx.x] : 0;
+
+  // Rows: lane column n of block qb is row qt*256 + wave*64 + qb*32 + n.
   const int wave_row0 = qt * kQTile + wave * kQW;
   const bool wave_active = wave_row0 < Lq;
   const int wave_last = min(wave_row0 + kQW - 1, Lq - 1);
@@ -129,180 +144,230 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   const int n_tiles = (kend_wg + kKTile - 1) / kKTile;
   const int tile_lo = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / a.n_splits);
   const int tile_hi = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / a.n_splits);
+  int kend[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int row = wave_row0 + qb * 32 + n;
+    const int qf = row < Lq ? row / T : a.n_q - 1;
+    kend[qb] = a.causal ? (first_q + qf + 1) * T : n_keys;
+  }
 
-  // ---- Q fragment: rotate in fp32, round to bf16 (B operand of S^T = K Q^T).
-  mfma_bf16x8 qfrag[D / 16];
+  // ---- Q fragments: rotate in fp32, round to bf16 (B operand of S^T = K Q^T).
+  mfma_bf16x8 qfrag[kQB][D / 16];
   {
     const double* freq_h = a.rope.freq + static_cast<size_t>(h) * (D / 2);
-    const int tok = row_ok ? row - qf * T : 0;
-    const int64_t t = a.frames.t[first_q + qf];
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) {
-        float x[8];
-        unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
-        rope_rotate8(a.rope, freq_h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
-        v = pack_bf16x8(x);
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int row = wave_row0 + qb * 32 + n;
+      const bool ok = row < Lq;
+      const int qf = ok ? row / T : 0;
+      const int tok = ok ? row - qf * T : 0;
+      const int64_t t = a.frames.t[first_q + qf];
+      const uint16_t* qrow =
+          static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * Lq + (ok ? row : 0)) * g.H + h) * D;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) {
+          float x[8];
+          unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
+          rope_rotate8(a.rope, freq_h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+          v = pack_bf16x8(x);
+        }
+        qfrag[qb][s] = as_bf16x8(v);
       }
-      qfrag[s] = as_bf16x8(v);
     }
   }
 
-  mfma_f32x16 oacc[D / 32];
+  mfma_f32x16 oacc[kQB][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = kNegInf;  // running max of scaled (log2-domain) scores
-  float l_run = 0.f;      // this half-wave's partial row sum
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
+  float m_run[kQB], l_run[kQB];  // running (lazy) max in log2 units; half-wave partial sums
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+  }
 
   const uint16_t* kst = static_cast<const uint16_t*>(g.k_store);
   const uint16_t* vst = static_cast<const uint16_t*>(g.v_store);
   const int64_t head_off = static_cast<int64_t>(b) * g.H + h;  // within a slot
   const int64_t slot_stride = static_cast<int64_t>(g.B) * g.H;
+  constexpr int CPR = D / 8;                      // K chunks per key row
+  constexpr int KVEC = kKTile * CPR / 256;        // K chunks per thread per tile
+  constexpr int VVEC = D * (kKTile / 8) / 256;    // V^T chunks per thread per tile
+  __syncthreads();  // s_slot visible
 
-  // Each thread moves 4 K vectors and 4 V^T vectors (16 B) per tile.
-  constexpr int KV = D / 8;                            // vectors per key row
-  constexpr int KVEC = kKTile * KV / 256;              // K vectors per thread
-  constexpr int VVEC = D * (kKTile / 8) / 256;         // V^T vectors per thread
-  u32x4 kreg[KVEC], vreg[VVEC];
-  auto load_tile = [&](int kt) {
+  // Global -> registers for one tile.  Keys past kend_wg are clamped to key 0
+  // (resident, finite): their scores are masked, so they contribute nothing.
+  auto load_tile = [&](int kt, u32x4* kr, u32x4* vr) {
     const int j0 = kt * kKTile;
+    int lf0 = 0, jb = 0;
+    const uint16_t *kb0 = kst, *kb1 = kst, *vb0 = vst, *vb1 = vst;
+    if (BIG_T) {
+      lf0 = j0 / T;
+      jb = (lf0 + 1) * T;
+      const int lf1 = min(lf0 + 1, n_res - 1);
+      const int64_t s0 = a.frames.store_slot[lf0], s1 = a.frames.store_slot[lf1];
+      kb0 = kst + ((s0 * slot_stride + head_off) * T - static_cast<int64_t>(lf0) * T) * D;
+      kb1 = kst + ((s1 * slot_stride + head_off) * T - static_cast<int64_t>(jb)) * D;
+      vb0 = vst + (s0 * slot_stride + head_off) * D * static_cast<int64_t>(T) - static_cast<int64_t>(lf0) * T;
+      vb1 = vst + (s1 * slot_stride + head_off) * D * static_cast<int64_t>(T) - static_cast<int64_t>(jb);
+    }
 #pragma unroll
     for (int u = 0; u < KVEC; ++u) {
       const int e = threadIdx.x + 256 * u;
-      const int r = e / KV, c = e % KV;
-      const int j = j0 + r;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < kend_wg) {
+      const int r = e / CPR, c = e % CPR;
+      int j = j0 + r;
+      if (j >= kend_wg) j = 0;
+      const uint16_t* src;
+      if (BIG_T) {
+        src = (j < jb && j >= lf0 * T) ? kb0 + static_cast<int64_t>(j) * D
+                                        : (j >= jb ? kb1 + static_cast<int64_t>(j) * D
+                                                   : kst + ((s_slot[0] * slot_stride + head_off) * T + j) * static_cast<int64_t>(D));
+      } else {
         const int lf = j / T;
-        const int tok = j - lf * T;
-        v = *reinterpret_cast<const u32x4*>(
-            kst + ((a.frames.store_slot[lf] * slot_stride + head_off) * T + tok) * static_cast<int64_t>(D) + c * 8);
+        src = kst + ((s_slot[lf] * slot_stride + head_off) * T + (j - lf * T)) * static_cast<int64_t>(D);
       }
-      kreg[u] = v;
+      kr[u] = *reinterpret_cast<const u32x4*>(src + c * 8);
     }
 #pragma unroll
     for (int u = 0; u < VVEC; ++u) {
       const int e = threadIdx.x + 256 * u;
-      const int d = e / (kKTile / 8), c = e % (kKTile / 8);
-      const int j = j0 + c * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < kend_wg) {
+      const int d = e / 8, c = e % 8;
+      int j = j0 + c * 8;
+      if (j >= kend_wg) j = 0;
+      const uint16_t* src;
+      if (BIG_T) {
+        src = (j < jb && j >= lf0 * T) ? vb0 + static_cast<int64_t>(d) * T + j
+                                        : (j >= jb ? vb1 + static_cast<int64_t>(d) * T + j
+                                                   : vst + ((s_slot[0] * slot_stride + head_off) * D + d) * static_cast<int64_t>(T) + j);
+      } else {
         const int lf = j / T;
-        const int tok = j - lf * T;
-        v = *reinterpret_cast<const u32x4*>(
-            vst + ((a.frames.store_slot[lf] * slot_stride + head_off) * D + d) * static_cast<int64_t>(T) + tok);
+        src = vst + ((s_slot[lf] * slot_stride + head_off) * D + d) * static_cast<int64_t>(T) + (j - lf * T);
       }
-      vreg[u] = v;
+      vr[u] = *reinterpret_cast<const u32x4*>(src);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](TileSmem<D>& st, const u32x4* kr, const u32x4* vr) {
 #pragma unroll
     for (int u = 0; u < KVEC; ++u) {
       const int e = threadIdx.x + 256 * u;
-      *reinterpret_cast<u32x4*>(&sm.k[buf][e / KV][(e % KV) * 8]) = kreg[u];
+      const int r = e / CPR, c = e % CPR;
+      st.k[r * CPR + (c ^ kswz<D>(r))] = kr[u];
     }
 #pragma unroll
     for (int u = 0; u < VVEC; ++u) {
       const int e = threadIdx.x + 256 * u;
-      *reinterpret_cast<u32x4*>(&sm.vt[buf][e / (kKTile / 8)][(e % (kKTile / 8)) * 8]) = vreg[u];
+      const int d = e / 8, c = e % 8;
+      st.vt[d * 8 + (c ^ vswz(d))] = vr[u];
     }
   };
 
-  if (tile_lo < tile_hi) {
-    load_tile(tile_lo);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int kt = tile_lo; kt < tile_hi; ++kt) {
-    const int buf = (kt - tile_lo) & 1;
+  // One 64-key tile = two 32-key blocks, each: S^T block (2 query blocks),
+  // softmax, then its half of O^T += V^T P^T.
+  auto compute = [&](int kt, const TileSmem<D>& st) {
     const int j0 = kt * kKTile;
-    if (kt + 1 < tile_hi) load_tile(kt + 1);  // in flight during this tile's math
-
-    if (wave_active && j0 < wave_kend) {
-      // ---- S^T = K Q^T for two 32-key blocks.
-      mfma_f32x16 sacc[2];
+    if (!(wave_active && j0 < wave_kend)) return;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
+      const int jb0 = j0 + kb * 32;
+      mfma_f32x16 sacc[kQB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-        const int krow = kb * 32 + key_perm(n);
+      for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const mfma_bf16x8 kf =
-              as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][krow][16 * s + 8 * hh]));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qfrag[s], sacc[kb], 0, 0, 0);
-        }
+        for (int i = 0; i < 16; ++i) sacc[qb][i] = 0.f;
+      const int krow = kb * 32 + key_perm(n);
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const mfma_bf16x8 kf = as_bf16x8(st.k[krow * CPR + ((2 * s + hh) ^ kswz<D>(krow))]);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qfrag[qb][s], sacc[qb], 0, 0, 0);
       }
 
-      // ---- mask (register i of block kb holds key j0 + 32kb + 16(i/8) + 8hh + i%8)
-      if (j0 + kKTile > kend) {
+      u32x4 pk[kQB][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < kQB; ++qb) {
+        // mask: register i holds key jb0 + 16(i/8) + 8hh + i%8
+        if (jb0 + 32 > kend[qb]) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = j0 + kb * 32 + 16 * (i >> 3) + 8 * hh + (i & 7);
-            if (key >= kend) sacc[kb][i] = kNegInf;
+            const int key = jb0 + 16 * (i >> 3) + 8 * hh + (i & 7);
+            if (key >= kend[qb]) sacc[qb][i] = kNegInf;
           }
-      }
-
-      // ---- online softmax (log2 domain), per lane = per query.
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
-      u32x4 pk[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], a.scale_log2, -m_use));
-          psum += p[i];
         }
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[qb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        // lazy max: raise it (and rescale) only when some row of the wave
+        // would otherwise see p > 2^kLazy
+        if (__any(mx > m_run[qb] + kLazy)) {
+          const float m_new = fmaxf(m_run[qb], mx);
+          const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+        }
+        const float m_use = m_run[qb] == kNegInf ? 0.f : m_run[qb];
+        float psum = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) pk[kb][s2][w] = cvt_pk_bf16(p[8 * s2 + 2 * w], p[8 * s2 + 2 * w + 1]);
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * s2 + 2 * w], a.scale_log2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * s2 + 2 * w + 1], a.scale_log2, -m_use));
+            psum += p0 + p1;
+            pk[qb][s2][w] = cvt_pk_bf16(p0, p1);
+          }
+        l_run[qb] += psum;
       }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T over this 32-key block
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
+        const int d = 32 * db + n;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const mfma_bf16x8 vf = as_bf16x8(st.vt[d * 8 + ((4 * kb + 2 * s2 + hh) ^ vswz(d))]);
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const mfma_bf16x8 vf = as_bf16x8(
-                *reinterpret_cast<const u32x4*>(&sm.vt[buf][32 * db + n][kb * 32 + 16 * s2 + 8 * hh]));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pk[kb][s2]), oacc[db],
-                                                               0, 0, 0);
-          }
+          for (int qb = 0; qb < kQB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pk[qb][s2]), oacc[qb][db],
+                                                                   0, 0, 0);
+        }
       }
     }
-    if (kt + 1 < tile_hi) store_tile(buf ^ 1);
+  };
+
+  // One register set in flight plus two LDS stages: while tile kt is read
+  // from one stage, tile kt+1 is fetched into registers and then written to
+  // the other stage.
+  u32x4 kr[KVEC], vr[VVEC];
+  if (tile_lo < tile_hi) {
+    load_tile(tile_lo, kr, vr);
+    store_tile(sm[0], kr, vr);
+  }
+  __syncthreads();
+  for (int kt = tile_lo; kt < tile_hi; ++kt) {
+    const int it = kt - tile_lo;
+    if (kt + 1 < tile_hi) load_tile(kt + 1, kr, vr);
+    compute(kt, sm[it & 1]);
+    if (kt + 1 < tile_hi) store_tile(sm[(it + 1) & 1], kr, vr);
     __syncthreads();
   }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32db + 8(i/4) + 4hh + i%4.
-  float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_tot[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
   if (a.n_splits > 1) {
     // Publish this split's partial, then the last-arriving split of the
     // q-tile merges all of them (fixed split order, so results are
@@ -310,19 +375,24 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     const int64_t plane = static_cast<int64_t>(g.B) * g.H * Lq;
     float* part_o = a.ws + kMaxTileCounters;
     float* part_ml = part_o + static_cast<int64_t>(a.n_splits) * plane * D;
-    const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
-    if (row_ok) {
-      float* po = part_o + (split * plane + prow) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int row = wave_row0 + qb * 32 + n;
+      if (row < Lq) {
+        const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
+        float* po = part_o + (split * plane + prow) * D;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 w = {oacc[db][4 * gq], oacc[db][4 * gq + 1], oacc[db][4 * gq + 2], oacc[db][4 * gq + 3]};
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x4 w = {oacc[qb][db][4 * gq], oacc[qb][db][4 * gq + 1], oacc[qb][db][4 * gq + 2],
+                             oacc[qb][db][4 * gq + 3]};
+            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
+          }
+        if (hh == 0) {
+          part_ml[(split * plane + prow) * 2] = m_run[qb];
+          part_ml[(split * plane + prow) * 2 + 1] = l_tot[qb];
         }
-      if (hh == 0) {
-        part_ml[(split * plane + prow) * 2] = m_run;
-        part_ml[(split * plane + prow) * 2 + 1] = l_tot;
       }
     }
     __threadfence();
@@ -337,43 +407,48 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     if (!s_last) return;
     __threadfence();
     if (threadIdx.x == 0) atomicExch(&counters[tile_id], 0);
-    if (!row_ok) return;
-    float M = kNegInf;
-    for (int s = 0; s < a.n_splits; ++s) {
-      const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
-      M = fmaxf(M, ms);
-    }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    l_tot = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-      const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
-      if (ms == kNegInf) continue;
-      const float w = __builtin_amdgcn_exp2f(ms - M);
-      l_tot += __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2 + 1]) * w;
-      const float* po = part_o + (s * plane + prow) * D;
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int row = wave_row0 + qb * 32 + n;
+      if (row >= Lq) continue;
+      const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
+      float M = kNegInf;
+      for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]));
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 32 * db + 8 * gq + 4 * hh));
+        for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
+      l_tot[qb] = 0.f;
+      for (int s = 0; s < a.n_splits; ++s) {
+        const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
+        if (ms == kNegInf) continue;
+        const float w = __builtin_amdgcn_exp2f(ms - M);
+        l_tot[qb] += __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2 + 1]) * w;
+        const float* po = part_o + (s * plane + prow) * D;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[db][4 * gq + i] += x[i] * w;
-        }
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 32 * db + 8 * gq + 4 * hh));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[qb][db][4 * gq + i] += x[i] * w;
+          }
+      }
     }
   }
-  if (row_ok) {
-    const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int row = wave_row0 + qb * 32 + n;
+    if (row >= Lq) continue;
+    const float inv = 1.f / l_tot[qb];
     uint16_t* orow = static_cast<uint16_t*>(a.o) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         uint2 w;
-        w.x = cvt_pk_bf16(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
-        w.y = cvt_pk_bf16(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
+        w.x = cvt_pk_bf16(oacc[qb][db][4 * gq] * inv, oacc[qb][db][4 * gq + 1] * inv);
+        w.y = cvt_pk_bf16(oacc[qb][db][4 * gq + 2] * inv, oacc[qb][db][4 * gq + 3] * inv);
         *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * hh) = w;
       }
   }
@@ -490,10 +565,10 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
     const int v = std::atoi(env);
     if (v >= 1) return static_cast<int>(v < max_s ? v : max_s);
   }
-  // Two workgroups fit a CU.  Pick the split count whose workgroup count
-  // best fills whole rounds of 2 x CUs, with a small charge per split for
-  // the partial results it writes and merges.
-  const double slots = 2.0 * num_cus;
+  // One workgroup per CU.  Pick the split count whose workgroup count best
+  // fills whole rounds of CUs, with a small charge per split for the partial
+  // results it writes and merges.
+  const double slots = 1.0 * num_cus;
   int best = 1;
   double best_score = -1.0;
   for (int64_t s = 1; s <= max_s; ++s) {
@@ -520,10 +595,14 @@ hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) 
   if (dtype == kBF16) {
     const int64_t wgs = static_cast<int64_t>((Lq + kQTile - 1) / kQTile) * BH * a.n_splits;
     const dim3 grid(static_cast<unsigned>(wgs));
-    if (a.g.D == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
+    const bool big_t = a.g.T >= kKTile;
+    if (a.g.D == 128) {
+      if (big_t) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, dim3(256), 0, stream, a);
+    } else {
+      if (big_t) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, dim3(256), 0, stream, a);
+    }
   } else {
     const dim3 grid((Lq + kF32Rows - 1) / kF32Rows, BH, 1);
     if (a.g.D == 128)
