@@ -122,8 +122,9 @@ sa_status sa_rope3d_apply(const sa_rope* rope, const void* x, void* y, sa_dtype 
  * Storage (library-internal layout, caller-allocated, borrowed):
  *   k_store: [n_sink + n_local][B][H][T_f][D]   keys, rotated at their frame time
  *   v_store: [n_sink + n_local][B][H][D][T_f]   values, transposed per (slot, b, h)
- * Each store is sa_cache_store_bytes(desc) bytes.  Use sa_cache_read to view a
- * frame in the boundary layout.
+ * Each store is sa_cache_store_bytes(desc) bytes and must be below 4 GiB (the
+ * kernels address a store with 32-bit byte offsets; larger caches fail with
+ * SA_ERR_SHAPE).  Use sa_cache_read to view a frame in the boundary layout.
  */
 typedef struct {
   int32_t batch;            /* B >= 1 */

@@ -235,6 +235,8 @@ sa_status sa_cache_create(const sa_cache_desc* d, const sa_rope* rope, sa_cache*
   // Every in-kernel index of one stream's queries and keys fits in int32.
   const long long keys = static_cast<long long>(d->n_sink + d->n_local) * d->tokens_per_frame;
   if (keys > (1LL << 30)) return fail(SA_ERR_SHAPE, "too many tokens in the window");
+  // The kernels address each store with 32-bit byte offsets.
+  if (sa_cache_store_bytes(d) > 0xFFFFFF00ull) return fail(SA_ERR_SHAPE, "each cache store must be below 4 GiB");
   sa_cache* c = new (std::nothrow) sa_cache();
   if (!c) return fail(SA_ERR_RANGE, "out of host memory");
   c->desc = *d;
@@ -350,6 +352,7 @@ sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q,
   a.scale_log2 = static_cast<float>(static_cast<double>(sc) * 1.4426950408889634);
   a.n_splits = splits;
   a.ws = static_cast<float*>(workspace);
+  a.store_bytes = static_cast<uint32_t>(sa_cache_store_bytes(&c->desc));
   const hipError_t e = sa::launch_window_attn(a, c->desc.dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();

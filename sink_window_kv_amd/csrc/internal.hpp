@@ -46,6 +46,7 @@ struct AttnArgs {
   float scale_log2;   // softmax scale * log2(e)
   int32_t n_splits;   // key splits (1 = no workspace)
   float* ws;          // split partials, see attn_workspace_bytes
+  uint32_t store_bytes;  // bytes of each cache store (< 4 GiB)
 };
 
 struct RecacheArgs {

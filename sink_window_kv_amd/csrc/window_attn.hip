@@ -202,55 +202,63 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
   constexpr int VVEC = D * (kKTile / 8) / 256;    // V^T chunks per thread per tile
   __syncthreads();  // s_slot visible
 
-  // Global -> registers for one tile.  Keys past kend_wg are clamped to key 0
-  // (resident, finite): their scores are masked, so they contribute nothing.
+  // Global -> registers for one tile, through buffer loads on the two stores
+  // (32-bit byte offsets; the descriptor bounds every access to its store).
+  // Keys past kend_wg are clamped to the tile's first key (resident, finite):
+  // their scores are masked, so they contribute nothing.
+  const uint32_t blk_elems = static_cast<uint32_t>(T) * D;  // one (slot, b, h) block
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kst), 0, static_cast<int>(a.store_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vst), 0, static_cast<int>(a.store_bytes), 0x00020000);
+  auto blk_bytes = [&](int lf) -> uint32_t {
+    return static_cast<uint32_t>((static_cast<int64_t>(a.frames.store_slot[lf]) * slot_stride + head_off) * blk_elems * 2);
+  };
   auto load_tile = [&](int kt, u32x4* kr, u32x4* vr) {
     const int j0 = kt * kKTile;
-    int lf0 = 0, jb = 0;
-    const uint16_t *kb0 = kst, *kb1 = kst, *vb0 = vst, *vb1 = vst;
+    uint32_t koff0 = 0, koff1 = 0, voff0 = 0, voff1 = 0;
+    int jb = 0;
     if (BIG_T) {
-      lf0 = j0 / T;
+      const int lf0 = j0 / T;
       jb = (lf0 + 1) * T;
       const int lf1 = min(lf0 + 1, n_res - 1);
-      const int64_t s0 = a.frames.store_slot[lf0], s1 = a.frames.store_slot[lf1];
-      kb0 = kst + ((s0 * slot_stride + head_off) * T - static_cast<int64_t>(lf0) * T) * D;
-      kb1 = kst + ((s1 * slot_stride + head_off) * T - static_cast<int64_t>(jb)) * D;
-      vb0 = vst + (s0 * slot_stride + head_off) * D * static_cast<int64_t>(T) - static_cast<int64_t>(lf0) * T;
-      vb1 = vst + (s1 * slot_stride + head_off) * D * static_cast<int64_t>(T) - static_cast<int64_t>(jb);
+      const uint32_t b0 = blk_bytes(lf0), b1 = blk_bytes(lf1);
+      koff0 = b0 - static_cast<uint32_t>(lf0) * blk_elems * 2;
+      koff1 = b1 - static_cast<uint32_t>(jb) * D * 2;
+      voff0 = b0 - static_cast<uint32_t>(lf0) * T * 2;
+      voff1 = b1 - static_cast<uint32_t>(jb) * 2;
     }
 #pragma unroll
     for (int u = 0; u < KVEC; ++u) {
       const int e = threadIdx.x + 256 * u;
       const int r = e / CPR, c = e % CPR;
       int j = j0 + r;
-      if (j >= kend_wg) j = 0;
-      const uint16_t* src;
+      if (j >= kend_wg) j = j0;
+      uint32_t off;
       if (BIG_T) {
-        src = (j < jb && j >= lf0 * T) ? kb0 + static_cast<int64_t>(j) * D
-                                        : (j >= jb ? kb1 + static_cast<int64_t>(j) * D
-                                                   : kst + ((s_slot[0] * slot_stride + head_off) * T + j) * static_cast<int64_t>(D));
+        off = (j < jb ? koff0 : koff1) + static_cast<uint32_t>(j) * (D * 2);
       } else {
         const int lf = j / T;
-        src = kst + ((s_slot[lf] * slot_stride + head_off) * T + (j - lf * T)) * static_cast<int64_t>(D);
+        off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
+              static_cast<uint32_t>(j - lf * T) * (D * 2);
       }
-      kr[u] = *reinterpret_cast<const u32x4*>(src + c * 8);
+      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off + c * 16, 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < VVEC; ++u) {
       const int e = threadIdx.x + 256 * u;
       const int d = e / 8, c = e % 8;
       int j = j0 + c * 8;
-      if (j >= kend_wg) j = 0;
-      const uint16_t* src;
+      if (j >= kend_wg) j = j0;
+      uint32_t off;
       if (BIG_T) {
-        src = (j < jb && j >= lf0 * T) ? vb0 + static_cast<int64_t>(d) * T + j
-                                        : (j >= jb ? vb1 + static_cast<int64_t>(d) * T + j
-                                                   : vst + ((s_slot[0] * slot_stride + head_off) * D + d) * static_cast<int64_t>(T) + j);
+        off = (j < jb ? voff0 : voff1) + static_cast<uint32_t>(d) * T * 2 + static_cast<uint32_t>(j) * 2;
       } else {
         const int lf = j / T;
-        src = vst + ((s_slot[lf] * slot_stride + head_off) * D + d) * static_cast<int64_t>(T) + (j - lf * T);
+        off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
+              static_cast<uint32_t>(d) * T * 2 + static_cast<uint32_t>(j - lf * T) * 2;
       }
-      vr[u] = *reinterpret_cast<const u32x4*>(src);
+      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
     }
   };
   auto store_tile = [&](TileSmem<D>& st, const u32x4* kr, const u32x4* vr) {
