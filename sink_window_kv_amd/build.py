@@ -27,6 +27,7 @@ CFLAGS = [
     # keep matrix-core accumulators in ordinary VGPRs where they fit (avoids
     # AGPR<->VGPR copies around the softmax, which reads the score tiles)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-Wno-inline-asm",  # the LDS-DMA asm names m0, which it sets itself
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

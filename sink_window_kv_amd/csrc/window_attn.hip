@@ -89,6 +89,39 @@ __device__ __forceinline__ int kswz(int r) {
 }
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
+// Raw buffer descriptor (gfx9 layout) over [base, base + bytes), in SGPRs.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32) & 0xffffu);  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);  // num_records: loads past the end return 0
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One 16-byte-per-lane global -> LDS transfer (buffer_load_dwordx4 ... lds):
+// lane L's chunk lands at lds_base + 16 L.  Written as inline asm so that the
+// compiler does not serialise it against reads of the other LDS stages (it
+// cannot prove they do not alias and would wait for every load in flight);
+// completion is tracked with explicit vmcnt waits instead.  The asm has no
+// output registers; M0 (the LDS base) is set inside the same block.
+__device__ __forceinline__ void dma16(const u32x4 rsrc, uint32_t voff, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_base)));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int D>
 struct TileSmem {
   u32x4 k[kKTile * D / 8];
@@ -111,7 +144,9 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
 // slot are resolved once per tile with scalar arithmetic.
 template <int D, bool BIG_T>
 __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
-  __shared__ TileSmem<D> sm[2];
+  // Three stages as three distinct objects, so the compiler can tell that
+  // the LDS-DMA into one stage does not alias the reads of another.
+  __shared__ TileSmem<D> st0, st1, st2;
   __shared__ int s_slot[kMaxFrames];
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
@@ -177,6 +212,13 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
         qfrag[qb][s] = as_bf16x8(v);
       }
     }
+    // The Q fragments are read-only matrix-core operands for the whole loop:
+    // keep them in AGPRs (the MFMA reads its B operand from there directly)
+    // and leave the VGPRs to the accumulators and the softmax.
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(qfrag[qb][s]));
   }
 
   mfma_f32x16 oacc[kQB][D / 32];
@@ -202,19 +244,22 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
   constexpr int VVEC = D * (kKTile / 8) / 256;    // V^T chunks per thread per tile
   __syncthreads();  // s_slot visible
 
-  // Global -> registers for one tile, through buffer loads on the two stores
-  // (32-bit byte offsets; the descriptor bounds every access to its store).
-  // Keys past kend_wg are clamped to the tile's first key (resident, finite):
-  // their scores are masked, so they contribute nothing.
+  // Global -> LDS for one tile by direct-to-LDS buffer loads (no VGPR
+  // staging): each wave instruction writes 64 consecutive 16-byte chunks, lane
+  // L landing at chunk (base + L); the lane fetches whichever global chunk the
+  // swizzled layout puts there.  32-bit byte offsets; the descriptor bounds
+  // every access to its store.  Keys past kend_wg are clamped to the tile's
+  // first key (resident, finite): their scores are masked, so they add nothing.
   const uint32_t blk_elems = static_cast<uint32_t>(T) * D;  // one (slot, b, h) block
-  const __amdgpu_buffer_rsrc_t krsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kst), 0, static_cast<int>(a.store_bytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vst), 0, static_cast<int>(a.store_bytes), 0x00020000);
+  const u32x4 krsrc = buffer_rsrc(kst, a.store_bytes);
+  const u32x4 vrsrc = buffer_rsrc(vst, a.store_bytes);
   auto blk_bytes = [&](int lf) -> uint32_t {
     return static_cast<uint32_t>((static_cast<int64_t>(a.frames.store_slot[lf]) * slot_stride + head_off) * blk_elems * 2);
   };
-  auto load_tile = [&](int kt, u32x4* kr, u32x4* vr) {
+  constexpr int KI = kKTile * CPR / 64 / kWaves;  // K wave-instructions per wave per tile
+  constexpr int VI = D * 8 / 64 / kWaves;         // V^T wave-instructions per wave per tile
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_tile = [&](int kt, TileSmem<D>& st) {
     const int j0 = kt * kKTile;
     uint32_t koff0 = 0, koff1 = 0, voff0 = 0, voff1 = 0;
     int jb = 0;
@@ -229,9 +274,10 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
       voff1 = b1 - static_cast<uint32_t>(jb) * 2;
     }
 #pragma unroll
-    for (int u = 0; u < KVEC; ++u) {
-      const int e = threadIdx.x + 256 * u;
-      const int r = e / CPR, c = e % CPR;
+    for (int u = 0; u < KI; ++u) {
+      const int i = wave_u * KI + u;
+      const int P = 64 * i + lane;
+      const int r = P / CPR, c = (P % CPR) ^ kswz<D>(r);
       int j = j0 + r;
       if (j >= kend_wg) j = j0;
       uint32_t off;
@@ -242,12 +288,13 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
         off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
               static_cast<uint32_t>(j - lf * T) * (D * 2);
       }
-      kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off + c * 16, 0, 0));
+      dma16(krsrc, off + c * 16, &st.k[64 * i]);
     }
 #pragma unroll
-    for (int u = 0; u < VVEC; ++u) {
-      const int e = threadIdx.x + 256 * u;
-      const int d = e / 8, c = e % 8;
+    for (int u = 0; u < VI; ++u) {
+      const int i = wave_u * VI + u;
+      const int P = 64 * i + lane;
+      const int d = P / 8, c = (P % 8) ^ vswz(d);
       int j = j0 + c * 8;
       if (j >= kend_wg) j = j0;
       uint32_t off;
@@ -258,21 +305,7 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
         off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
               static_cast<uint32_t>(d) * T * 2 + static_cast<uint32_t>(j - lf * T) * 2;
       }
-      vr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
-    }
-  };
-  auto store_tile = [&](TileSmem<D>& st, const u32x4* kr, const u32x4* vr) {
-#pragma unroll
-    for (int u = 0; u < KVEC; ++u) {
-      const int e = threadIdx.x + 256 * u;
-      const int r = e / CPR, c = e % CPR;
-      st.k[r * CPR + (c ^ kswz<D>(r))] = kr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VVEC; ++u) {
-      const int e = threadIdx.x + 256 * u;
-      const int d = e / 8, c = e % 8;
-      st.vt[d * 8 + (c ^ vswz(d))] = vr[u];
+      dma16(vrsrc, off, &st.vt[64 * i]);
     }
   };
 
@@ -355,21 +388,28 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // One register set in flight plus two LDS stages: while tile kt is read
-  // from one stage, tile kt+1 is fetched into registers and then written to
-  // the other stage.
-  u32x4 kr[KVEC], vr[VVEC];
-  if (tile_lo < tile_hi) {
-    load_tile(tile_lo, kr, vr);
-    store_tile(sm[0], kr, vr);
-  }
-  __syncthreads();
-  for (int kt = tile_lo; kt < tile_hi; ++kt) {
-    const int it = kt - tile_lo;
-    if (kt + 1 < tile_hi) load_tile(kt + 1, kr, vr);
-    compute(kt, sm[it & 1]);
-    if (kt + 1 < tile_hi) store_tile(sm[(it + 1) & 1], kr, vr);
-    __syncthreads();
+  // Three-stage pipeline, unrolled by three so every stage is a fixed
+  // object: at step kt, wait for tile kt's loads (tile kt+1 may stay in
+  // flight), barrier (which also retires the stage computed at step kt-1),
+  // issue tile kt+2 into that retired stage, compute tile kt.
+  constexpr int kLoadsPerTile = KI + VI;  // per thread
+  auto step = [&](int kt, TileSmem<D>& cur, TileSmem<D>& nxt2) {
+    if (kt + 1 < tile_hi) wait_vmcnt<kLoadsPerTile>();
+    else wait_vmcnt<0>();
+    // Plain s_barrier: a __syncthreads() fence would wait for every load in
+    // flight (vmcnt(0)), including the next tile's.  The explicit vmcnt wait
+    // above covers this tile; the "memory" clobber keeps the compiler from
+    // moving LDS accesses across the barrier.
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 2 < tile_hi) issue_tile(kt + 2, nxt2);
+    compute(kt, cur);
+  };
+  if (tile_lo < tile_hi) issue_tile(tile_lo, st0);
+  if (tile_lo + 1 < tile_hi) issue_tile(tile_lo + 1, st1);
+  for (int kt = tile_lo; kt < tile_hi; kt += 3) {
+    step(kt, st0, st2);
+    if (kt + 1 < tile_hi) step(kt + 1, st1, st0);
+    if (kt + 2 < tile_hi) step(kt + 2, st2, st1);
   }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32db + 8(i/4) + 4hh + i%4.
