@@ -9,22 +9,27 @@
 // increasing frame order, every query row sees a prefix [0, kend) of the
 // logical key sequence.
 //
-// bf16 kernel (gfx950 matrix cores), per workgroup of 4 waves:
-//   * each wave owns 32 query rows; the wave computes S^T = K Q^T with
-//     v_mfma_f32_32x32x16_bf16 so that every lane holds the scores of ONE
-//     query (column) for 16 keys per 32-key block -- the row max and row sum
-//     are in-lane plus one exchange between the two half-waves;
-//   * the keys of each 32-key block are permuted (bits 2 and 3 of the row
-//     index swapped) when the K operand is read from LDS, so that the score
+// bf16 kernel (gfx950 matrix cores).  A workgroup of 4 waves owns 128 query
+// rows of one (stream, head); two workgroups share a CU, so each SIMD runs
+// two waves from different workgroups and one wave's softmax overlaps the
+// other's matrix-core work.
+//   * Each wave owns 32 query rows and computes S^T = K Q^T with
+//     v_mfma_f32_32x32x16_bf16, so that every lane holds the scores of ONE
+//     query (column) for 16 keys per 32-key block: the row max and row sum are
+//     in-lane plus one exchange between the two half-waves.
+//   * The keys of each 32-key block are permuted (bits 2 and 3 of the row
+//     index swapped) when the K operand is read from LDS, so the score
 //     registers are already in the order the P^T operand of the second
-//     product needs: O^T += V^T P^T runs straight from registers;
-//   * V is stored transposed in the cache ([D][T] per slot, stream, head), so
-//     the V^T operand is a plain 16-byte LDS read;
-//   * q is rotated (RoPE) in fp32 as it is loaded, then rounded to bf16;
-//   * online softmax in the exp2 domain, fp32 statistics;
-//   * K and V^T tiles of 64 keys are staged in LDS; per-key addresses come
-//     from the per-frame slot table, so sink and ring frames are read in
-//     place with no gather copy.
+//     product needs: O^T += V^T P^T runs straight from registers.
+//   * V is stored transposed in the cache ([D][T] per slot, stream and head),
+//     so the V^T operand is a plain 16-byte LDS read.
+//   * q is rotated (RoPE) in fp32 as it is loaded, then rounded to bf16.
+//   * Online softmax in the exp2 domain with a lazily raised running max; the
+//     row sum is accumulated from the same bf16-rounded p the PV product uses.
+//   * K and V^T tiles of 64 keys go global -> LDS by direct-to-LDS buffer
+//     loads into two XOR-swizzled stages (no VGPR staging, conflict-free
+//     operand reads); per-tile frame bases come from the slot table, so sink
+//     and ring frames are read in place with no gather copy.
 // For one stream at Wan-1.3B shapes the (q-tile, head) grid alone does not
 // fill 256 CUs, so the key range is split; each split publishes a partial
 // (O, m, l) and the last split of a q-tile to arrive (atomic counter) merges
@@ -44,33 +49,17 @@ namespace {
 
 typedef __bf16 mfma_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float mfma_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-constexpr int kQB = 2;                  // 32-row query blocks per wave
-constexpr int kQW = 32 * kQB;           // query rows per wave
+constexpr int kQW = 32;                 // query rows per wave
 constexpr int kQTile = kWaves * kQW;    // query rows per workgroup
-constexpr int kKTile = 64;              // keys per iteration
+constexpr int kKTile = 64;              // keys per LDS stage
 constexpr float kNegInf = -__builtin_huge_valf();
 // Lazy rescaling: the running max used for exp2 is only raised when a new
 // score exceeds it by more than this (log2 units), so p <= 2^kLazy.
 constexpr float kLazy = 8.f;
-
-__device__ __forceinline__ int key_perm(int m) {  // swap bits 2 and 3
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-__device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) {
-  return __builtin_bit_cast(mfma_bf16x8, v);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> packed bf16x2 with the hardware converter (round to nearest even).
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 // Workspace layout (float units): [0, 1024) int32 arrival counters, one per
 // (stream, head, q-tile); then split partials O [S][B][H][Lq][D] (fp32,
@@ -79,15 +68,23 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // counter, so every call leaves them zero again.
 constexpr int kMaxTileCounters = 1024;
 
-// LDS tile layout (16-byte chunks, no padding, XOR-swizzled so that the 16
-// lanes of a matrix-core operand read hit 16 distinct bank groups):
-//   K   : 64 keys x (D/8) chunks, chunk (r, c) at r*(D/8) + (c ^ kswz(r))
-//   V^T : D rows x 8 chunks (8 keys each), chunk (d, c) at d*8 + (c ^ vswz(d))
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+__device__ __forceinline__ int key_perm(int m) {  // swap bits 2 and 3
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+__device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(mfma_bf16x8, v); }
+
+// Two fp32 -> packed bf16x2 with the hardware converter (round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Sum of the two bf16 halves of a packed word, accumulated in fp32.
+__device__ __forceinline__ float dot2_ones(uint32_t pk, float acc) {
+  const bf16x2_t one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
+}
 
 // Raw buffer descriptor (gfx9 layout) over [base, base + bytes), in SGPRs.
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
@@ -102,7 +99,7 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 
 // One 16-byte-per-lane global -> LDS transfer (buffer_load_dwordx4 ... lds):
 // lane L's chunk lands at lds_base + 16 L.  Written as inline asm so that the
-// compiler does not serialise it against reads of the other LDS stages (it
+// compiler does not serialise it against reads of the other LDS stage (it
 // cannot prove they do not alias and would wait for every load in flight);
 // completion is tracked with explicit vmcnt waits instead.  The asm has no
 // output registers; M0 (the LDS base) is set inside the same block.
@@ -115,15 +112,25 @@ __device__ __forceinline__ void dma16(const u32x4 rsrc, uint32_t voff, const voi
                : "memory", "m0");
 }
 
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Plain s_barrier: a __syncthreads() fence would also wait for every load in
+// flight.  The "memory" clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS stage: 16-byte chunks, no padding, XOR-swizzled so that the 16 lanes of
+// a matrix-core operand read hit 16 distinct bank groups:
+//   K   : 64 keys x (D/8) chunks, chunk (r, c) at r*(D/8) + (c ^ kswz(r))
+//   V^T : D rows x 8 chunks (8 keys each), chunk (d, c) at d*8 + (c ^ vswz(d))
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
 template <int D>
-struct TileSmem {
+struct StageSmem {
   u32x4 k[kKTile * D / 8];
   u32x4 vt[D * kKTile / 8];
 };
@@ -140,17 +147,26 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
+template <int D>
+__device__ __forceinline__ u32x4 lds_read(const StageSmem<D>& st, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&st) + byte_off);
+}
+
 // BIG_T: every 64-key tile spans at most two frames (T >= 64), so frame and
-// slot are resolved once per tile with scalar arithmetic.
+// slot are resolved once per tile with uniform arithmetic.
 template <int D, bool BIG_T>
-__global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
-  // Three stages as three distinct objects, so the compiler can tell that
-  // the LDS-DMA into one stage does not alias the reads of another.
-  __shared__ TileSmem<D> st0, st1, st2;
+__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
+  __shared__ StageSmem<D> st0, st1;
   __shared__ int s_slot[kMaxFrames];
   __shared__ int s_last;
+  constexpr int CPR = D / 8;                      // K chunks per key row
+  constexpr int KI = kKTile * CPR / 64 / kWaves;  // K DMA instructions per wave per tile
+  constexpr int VI = D * 8 / 64 / kWaves;         // V^T DMA instructions per wave per tile
+  constexpr uint32_t kVtOff = kKTile * D * 2;     // byte offset of vt inside a stage
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int n = lane & 31;
   const int hh = lane >> 5;
   const CacheGeom& g = a.g;
@@ -169,97 +185,80 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
   const int n_keys = n_res * T;
   if (threadIdx.x < kMaxFrames) s_slot[threadIdx.x] = threadIdx.x < n_res ? a.frames.store_slot[threadIdx.x] : 0;
 
-  // Rows: lane column n of block qb is row qt*256 + wave*64 + qb*32 + n.
+  const int row = qt * kQTile + wave * kQW + n;
+  const bool row_ok = row < Lq;
+  const int qf = row_ok ? row / T : a.n_q - 1;
+  const int kend = a.causal ? (first_q + qf + 1) * T : n_keys;
   const int wave_row0 = qt * kQTile + wave * kQW;
   const bool wave_active = wave_row0 < Lq;
   const int wave_last = min(wave_row0 + kQW - 1, Lq - 1);
-  const int wave_kend = a.causal ? (first_q + wave_last / T + 1) * T : n_keys;
+  const int wave_kend = a.causal ? (first_q + wave_last / T + 1) * T : n_keys;            // largest kend
+  const int wave_kmin = a.causal ? (first_q + min(wave_row0, Lq - 1) / T + 1) * T : n_keys;  // smallest
   const int last_row = min(qt * kQTile + kQTile - 1, Lq - 1);
   const int kend_wg = a.causal ? (first_q + last_row / T + 1) * T : n_keys;
   const int n_tiles = (kend_wg + kKTile - 1) / kKTile;
   const int tile_lo = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / a.n_splits);
   const int tile_hi = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / a.n_splits);
-  int kend[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int row = wave_row0 + qb * 32 + n;
-    const int qf = row < Lq ? row / T : a.n_q - 1;
-    kend[qb] = a.causal ? (first_q + qf + 1) * T : n_keys;
-  }
 
-  // ---- Q fragments: rotate in fp32, round to bf16 (B operand of S^T = K Q^T).
-  mfma_bf16x8 qfrag[kQB][D / 16];
+  // ---- Q fragment: rotate in fp32, round to bf16 (B operand of S^T = K Q^T).
+  mfma_bf16x8 qfrag[D / 16];
   {
     const double* freq_h = a.rope.freq + static_cast<size_t>(h) * (D / 2);
+    const int tok = row_ok ? row - qf * T : 0;
+    const int64_t t = a.frames.t[first_q + qf];
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * Lq + (row_ok ? row : 0)) * g.H + h) * D;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int row = wave_row0 + qb * 32 + n;
-      const bool ok = row < Lq;
-      const int qf = ok ? row / T : 0;
-      const int tok = ok ? row - qf * T : 0;
-      const int64_t t = a.frames.t[first_q + qf];
-      const uint16_t* qrow =
-          static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * Lq + (ok ? row : 0)) * g.H + h) * D;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok) {
-          float x[8];
-          unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
-          rope_rotate8(a.rope, freq_h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
-          v = pack_bf16x8(x);
-        }
-        qfrag[qb][s] = as_bf16x8(v);
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) {
+        float x[8];
+        unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
+        rope_rotate8(a.rope, freq_h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+        v = pack_bf16x8(x);
       }
+      qfrag[s] = as_bf16x8(v);
     }
-    // The Q fragments are read-only matrix-core operands for the whole loop:
-    // keep them in AGPRs (the MFMA reads its B operand from there directly)
-    // and leave the VGPRs to the accumulators and the softmax.
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) asm volatile("" : "+a"(qfrag[qb][s]));
   }
 
-  mfma_f32x16 oacc[kQB][D / 32];
+  mfma_f32x16 oacc[D / 32];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
-  float m_run[kQB], l_run[kQB];  // running (lazy) max in log2 units; half-wave partial sums
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    m_run[qb] = kNegInf;
-    l_run[qb] = 0.f;
-  }
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = kNegInf;  // running (lazy) max of scaled scores, log2 units
+  float l_run = 0.f;      // this half-wave's partial row sum
 
+  // Per-lane LDS operand addresses (bytes inside a stage); the key block,
+  // channel block and stage enter as immediate offsets.
+  uint32_t kaddr[D / 16];
+  {
+    const int r = key_perm(n);  // key row inside the 32-key block (kb adds 32 rows)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) kaddr[s] = static_cast<uint32_t>((r * CPR + ((2 * s + hh) ^ kswz<D>(r))) * 16);
+  }
+  uint32_t vaddr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) vaddr[q] = kVtOff + static_cast<uint32_t>((n * 8 + (((q << 1) | hh) ^ vswz(n))) * 16);
+
+  // ---- global -> LDS (direct) for one tile.
   const uint16_t* kst = static_cast<const uint16_t*>(g.k_store);
   const uint16_t* vst = static_cast<const uint16_t*>(g.v_store);
   const int64_t head_off = static_cast<int64_t>(b) * g.H + h;  // within a slot
   const int64_t slot_stride = static_cast<int64_t>(g.B) * g.H;
-  constexpr int CPR = D / 8;                      // K chunks per key row
-  constexpr int KVEC = kKTile * CPR / 256;        // K chunks per thread per tile
-  constexpr int VVEC = D * (kKTile / 8) / 256;    // V^T chunks per thread per tile
-  __syncthreads();  // s_slot visible
-
-  // Global -> LDS for one tile by direct-to-LDS buffer loads (no VGPR
-  // staging): each wave instruction writes 64 consecutive 16-byte chunks, lane
-  // L landing at chunk (base + L); the lane fetches whichever global chunk the
-  // swizzled layout puts there.  32-bit byte offsets; the descriptor bounds
-  // every access to its store.  Keys past kend_wg are clamped to the tile's
-  // first key (resident, finite): their scores are masked, so they add nothing.
   const uint32_t blk_elems = static_cast<uint32_t>(T) * D;  // one (slot, b, h) block
   const u32x4 krsrc = buffer_rsrc(kst, a.store_bytes);
   const u32x4 vrsrc = buffer_rsrc(vst, a.store_bytes);
+  __syncthreads();  // s_slot visible
   auto blk_bytes = [&](int lf) -> uint32_t {
-    return static_cast<uint32_t>((static_cast<int64_t>(a.frames.store_slot[lf]) * slot_stride + head_off) * blk_elems * 2);
+    const int slot = __builtin_amdgcn_readfirstlane(s_slot[lf]);
+    return static_cast<uint32_t>((static_cast<int64_t>(slot) * slot_stride + head_off) * blk_elems * 2);
   };
-  constexpr int KI = kKTile * CPR / 64 / kWaves;  // K wave-instructions per wave per tile
-  constexpr int VI = D * 8 / 64 / kWaves;         // V^T wave-instructions per wave per tile
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_tile = [&](int kt, TileSmem<D>& st) {
+  // Each wave instruction writes 64 consecutive chunks of the stage, lane L
+  // landing at chunk (base + L); the lane fetches whichever global chunk the
+  // swizzled layout puts there.  Keys past kend_wg are clamped to the tile's
+  // first key (resident, finite): their scores are masked, they add nothing.
+  auto issue_tile = [&](int kt, StageSmem<D>& st) {
     const int j0 = kt * kKTile;
     uint32_t koff0 = 0, koff1 = 0, voff0 = 0, voff1 = 0;
     int jb = 0;
@@ -309,113 +308,86 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // One 64-key tile = two 32-key blocks, each: S^T block (2 query blocks),
-  // softmax, then its half of O^T += V^T P^T.
-  auto compute = [&](int kt, const TileSmem<D>& st) {
+  // ---- one 64-key tile: S^T for both 32-key blocks (two independent
+  // accumulation chains), softmax of the 32 scores each lane holds, then
+  // O^T += V^T P^T over four channel blocks.
+  auto compute = [&](int kt, const StageSmem<D>& st) {
     const int j0 = kt * kKTile;
-    if (!(wave_active && j0 < wave_kend)) return;
+    if (!wave_active || j0 >= wave_kend) return;
+    mfma_f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int jb0 = j0 + kb * 32;
-      mfma_f32x16 sacc[kQB];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[qb][i] = 0.f;
-      const int krow = kb * 32 + key_perm(n);
+    for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const mfma_bf16x8 kf = as_bf16x8(st.k[krow * CPR + ((2 * s + hh) ^ kswz<D>(krow))]);
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read(st, kaddr[s] + kb * 32 * CPR * 16)),
+                                                            qfrag[s], sacc[kb], 0, 0, 0);
+    // mask (register i of block kb holds key j0 + 32kb + 16(i/8) + 8hh + i%8)
+    if (j0 + kKTile > wave_kmin) {
+      const int lim = kend - j0 - 8 * hh;  // keys j0 + 8hh + off with off >= lim are hidden
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qfrag[qb][s], sacc[qb], 0, 0, 0);
-      }
-
-      u32x4 pk[kQB][2];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        // mask: register i holds key jb0 + 16(i/8) + 8hh + i%8
-        if (jb0 + 32 > kend[qb]) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = jb0 + 16 * (i >> 3) + 8 * hh + (i & 7);
-            if (key >= kend[qb]) sacc[qb][i] = kNegInf;
-          }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[qb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-        // lazy max: raise it (and rescale) only when some row of the wave
-        // would otherwise see p > 2^kLazy
-        if (__any(mx > m_run[qb] + kLazy)) {
-          const float m_new = fmaxf(m_run[qb], mx);
-          const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
-        }
-        const float m_use = m_run[qb] == kNegInf ? 0.f : m_run[qb];
-        float psum = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * s2 + 2 * w], a.scale_log2, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * s2 + 2 * w + 1], a.scale_log2, -m_use));
-            psum += p0 + p1;
-            pk[qb][s2][w] = cvt_pk_bf16(p0, p1);
-          }
-        l_run[qb] += psum;
-      }
-
-      // ---- O^T += V^T P^T over this 32-key block
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + n;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const mfma_bf16x8 vf = as_bf16x8(st.vt[d * 8 + ((4 * kb + 2 * s2 + hh) ^ vswz(d))]);
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, as_bf16x8(pk[qb][s2]), oacc[qb][db],
-                                                                   0, 0, 0);
-        }
-      }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 16 * (i >> 3) + (i & 7) >= lim) sacc[kb][i] = kNegInf;
     }
+    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    u32x4 pk[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * s2 + 2 * w], a.scale_log2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * s2 + 2 * w + 1], a.scale_log2, -m_use));
+          pk[kb][s2][w] = cvt_pk_bf16(p0, p1);
+          l_run = dot2_ones(pk[kb][s2][w], l_run);
+        }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(lds_read(st, vaddr[q] + db * 32 * 8 * 16)), as_bf16x8(pk[q >> 1][q & 1]), oacc[db], 0, 0, 0);
   };
 
-  // Three-stage pipeline, unrolled by three so every stage is a fixed
-  // object: at step kt, wait for tile kt's loads (tile kt+1 may stay in
-  // flight), barrier (which also retires the stage computed at step kt-1),
-  // issue tile kt+2 into that retired stage, compute tile kt.
-  constexpr int kLoadsPerTile = KI + VI;  // per thread
-  auto step = [&](int kt, TileSmem<D>& cur, TileSmem<D>& nxt2) {
-    if (kt + 1 < tile_hi) wait_vmcnt<kLoadsPerTile>();
-    else wait_vmcnt<0>();
-    // Plain s_barrier: a __syncthreads() fence would wait for every load in
-    // flight (vmcnt(0)), including the next tile's.  The explicit vmcnt wait
-    // above covers this tile; the "memory" clobber keeps the compiler from
-    // moving LDS accesses across the barrier.
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + 2 < tile_hi) issue_tile(kt + 2, nxt2);
-    compute(kt, cur);
-  };
+  // ---- two-stage pipeline, unrolled by two so both stages are fixed
+  // objects: wait for tile kt, barrier (which also retires the stage read at
+  // kt-1), issue tile kt+1 into that stage, compute tile kt.
   if (tile_lo < tile_hi) issue_tile(tile_lo, st0);
-  if (tile_lo + 1 < tile_hi) issue_tile(tile_lo + 1, st1);
-  for (int kt = tile_lo; kt < tile_hi; kt += 3) {
-    step(kt, st0, st2);
-    if (kt + 1 < tile_hi) step(kt + 1, st1, st0);
-    if (kt + 2 < tile_hi) step(kt + 2, st2, st1);
+  for (int kt = tile_lo; kt < tile_hi; kt += 2) {
+    wait_vmcnt0();
+    barrier();
+    if (kt + 1 < tile_hi) issue_tile(kt + 1, st1);
+    compute(kt, st0);
+    if (kt + 1 < tile_hi) {
+      wait_vmcnt0();
+      barrier();
+      if (kt + 2 < tile_hi) issue_tile(kt + 2, st0);
+      compute(kt + 1, st1);
+    }
   }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32db + 8(i/4) + 4hh + i%4.
-  float l_tot[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
+  float l_tot = l_run + __shfl_xor(l_run, 32);
   if (a.n_splits > 1) {
     // Publish this split's partial, then the last-arriving split of the
     // q-tile merges all of them (fixed split order, so results are
@@ -423,24 +395,19 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
     const int64_t plane = static_cast<int64_t>(g.B) * g.H * Lq;
     float* part_o = a.ws + kMaxTileCounters;
     float* part_ml = part_o + static_cast<int64_t>(a.n_splits) * plane * D;
+    const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
+    if (row_ok) {
+      float* po = part_o + (split * plane + prow) * D;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int row = wave_row0 + qb * 32 + n;
-      if (row < Lq) {
-        const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
-        float* po = part_o + (split * plane + prow) * D;
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const f32x4 w = {oacc[qb][db][4 * gq], oacc[qb][db][4 * gq + 1], oacc[qb][db][4 * gq + 2],
-                             oacc[qb][db][4 * gq + 3]};
-            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
-          }
-        if (hh == 0) {
-          part_ml[(split * plane + prow) * 2] = m_run[qb];
-          part_ml[(split * plane + prow) * 2 + 1] = l_tot[qb];
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 w = {oacc[db][4 * gq], oacc[db][4 * gq + 1], oacc[db][4 * gq + 2], oacc[db][4 * gq + 3]};
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
         }
+      if (hh == 0) {
+        part_ml[(split * plane + prow) * 2] = m_run;
+        part_ml[(split * plane + prow) * 2 + 1] = l_tot;
       }
     }
     __threadfence();
@@ -455,48 +422,40 @@ __global__ void __launch_bounds__(256, 1) attn_bf16_kernel(AttnArgs a) {
     if (!s_last) return;
     __threadfence();
     if (threadIdx.x == 0) atomicExch(&counters[tile_id], 0);
+    if (!row_ok) return;
+    float M = kNegInf;
+    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]));
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int row = wave_row0 + qb * 32 + n;
-      if (row >= Lq) continue;
-      const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
-      float M = kNegInf;
-      for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]));
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    l_tot = 0.f;
+    for (int s = 0; s < a.n_splits; ++s) {
+      const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
+      if (ms == kNegInf) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - M);
+      l_tot += __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2 + 1]) * w;
+      const float* po = part_o + (s * plane + prow) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
-      l_tot[qb] = 0.f;
-      for (int s = 0; s < a.n_splits; ++s) {
-        const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
-        if (ms == kNegInf) continue;
-        const float w = __builtin_amdgcn_exp2f(ms - M);
-        l_tot[qb] += __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2 + 1]) * w;
-        const float* po = part_o + (s * plane + prow) * D;
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 32 * db + 8 * gq + 4 * hh));
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 32 * db + 8 * gq + 4 * hh));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) oacc[qb][db][4 * gq + i] += x[i] * w;
-          }
-      }
+          for (int i = 0; i < 4; ++i) oacc[db][4 * gq + i] += x[i] * w;
+        }
     }
   }
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int row = wave_row0 + qb * 32 + n;
-    if (row >= Lq) continue;
-    const float inv = 1.f / l_tot[qb];
+  if (row_ok) {
+    const float inv = 1.f / l_tot;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         uint2 w;
-        w.x = cvt_pk_bf16(oacc[qb][db][4 * gq] * inv, oacc[qb][db][4 * gq + 1] * inv);
-        w.y = cvt_pk_bf16(oacc[qb][db][4 * gq + 2] * inv, oacc[qb][db][4 * gq + 3] * inv);
+        w.x = cvt_pk_bf16(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
+        w.y = cvt_pk_bf16(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
         *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * hh) = w;
       }
   }
@@ -613,10 +572,10 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
     const int v = std::atoi(env);
     if (v >= 1) return static_cast<int>(v < max_s ? v : max_s);
   }
-  // One workgroup per CU.  Pick the split count whose workgroup count best
-  // fills whole rounds of CUs, with a small charge per split for the partial
-  // results it writes and merges.
-  const double slots = 1.0 * num_cus;
+  // Two workgroups share a CU.  Pick the split count whose workgroup count
+  // best fills whole rounds of 2 x CUs, with a small charge per split for the
+  // partial results it writes and merges.
+  const double slots = 2.0 * num_cus;
   int best = 1;
   double best_score = -1.0;
   for (int64_t s = 1; s <= max_s; ++s) {
