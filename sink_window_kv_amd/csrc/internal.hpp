@@ -47,6 +47,7 @@ struct AttnArgs {
   int32_t n_splits;   // key splits (1 = no workspace)
   float* ws;          // split partials, see attn_workspace_bytes
   uint32_t store_bytes;  // bytes of each cache store (< 4 GiB)
+  int32_t n_waves;       // waves per workgroup (bf16 kernel)
 };
 
 struct RecacheArgs {
@@ -68,7 +69,8 @@ hipError_t launch_append(const RopeArgs& rope, const CacheGeom& g, const void* k
 hipError_t launch_read(const CacheGeom& g, int store_slot, void* k_out, void* v_out, int dtype,
                        hipStream_t stream);
 
-// Number of key splits the attention launch uses for this shape.
+// Waves per workgroup and number of key splits the attention launch uses.
+int attn_waves(int dtype, int B, int H, int D, int T, int n_q);
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus);
 size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits);
 hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream);

@@ -52,9 +52,7 @@ typedef float mfma_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
 constexpr int kQW = 32;                 // query rows per wave
-constexpr int kQTile = kWaves * kQW;    // query rows per workgroup
 constexpr int kKTile = 64;              // keys per LDS stage
 constexpr float kNegInf = -__builtin_huge_valf();
 // Lazy rescaling: the running max used for exp2 is only raised when a new
@@ -154,8 +152,12 @@ __device__ __forceinline__ u32x4 lds_read(const StageSmem<D>& st, uint32_t byte_
 
 // BIG_T: every 64-key tile spans at most two frames (T >= 64), so frame and
 // slot are resolved once per tile with uniform arithmetic.
-template <int D, bool BIG_T>
-__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
+// W waves per workgroup (W * 32 query rows).  W = 4: two workgroups per CU;
+// W = 8: one workgroup per CU, half the K/V traffic per query row.
+template <int D, bool BIG_T, int W>
+__global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
+  constexpr int kWaves = W;
+  constexpr int kQTile = W * kQW;  // query rows per workgroup
   __shared__ StageSmem<D> st0, st1;
   __shared__ int s_slot[kMaxFrames];
   __shared__ int s_last;
@@ -559,10 +561,20 @@ __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus) {
-  (void)D;
+int attn_waves(int dtype, int B, int H, int D, int T, int n_q) {
+  (void)B; (void)H; (void)D; (void)T; (void)n_q;
   if (dtype != kBF16) return 1;
-  const int64_t tiles = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + kQTile - 1) / kQTile);
+  if (const char* env = std::getenv("SA_ATTN_WAVES")) {
+    if (std::atoi(env) == 4) return 4;
+  }
+  return 8;
+}
+
+int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus) {
+  if (dtype != kBF16) return 1;
+  const int W = attn_waves(dtype, B, H, D, T, n_q);
+  const int64_t q_tile = 32LL * W;
+  const int64_t tiles = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + q_tile - 1) / q_tile);
   const int64_t key_tiles = (static_cast<int64_t>(n_res) * T + kKTile - 1) / kKTile;
   if (tiles > kMaxTileCounters) return 1;
   int64_t max_s = key_tiles / 8;  // at least 8 key tiles per split
@@ -572,10 +584,10 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
     const int v = std::atoi(env);
     if (v >= 1) return static_cast<int>(v < max_s ? v : max_s);
   }
-  // Two workgroups share a CU.  Pick the split count whose workgroup count
-  // best fills whole rounds of 2 x CUs, with a small charge per split for the
-  // partial results it writes and merges.
-  const double slots = 2.0 * num_cus;
+  // Pick the split count whose workgroup count best fills whole rounds of
+  // the CUs' workgroup slots, with a small charge per split for the partial
+  // results it writes and merges.
+  const double slots = static_cast<double>(num_cus) * (W == 4 ? 2 : 1);
   int best = 1;
   double best_score = -1.0;
   for (int64_t s = 1; s <= max_s; ++s) {
@@ -600,16 +612,20 @@ hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) 
   const int Lq = a.n_q * a.g.T;
   const int BH = a.g.B * a.g.H;
   if (dtype == kBF16) {
-    const int64_t wgs = static_cast<int64_t>((Lq + kQTile - 1) / kQTile) * BH * a.n_splits;
+    const int W = a.n_waves;
+    const int64_t wgs = static_cast<int64_t>((Lq + 32 * W - 1) / (32 * W)) * BH * a.n_splits;
     const dim3 grid(static_cast<unsigned>(wgs));
+    const dim3 block(64 * W);
     const bool big_t = a.g.T >= kKTile;
-    if (a.g.D == 128) {
-      if (big_t) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, dim3(256), 0, stream, a);
+#define SA_LAUNCH_ATTN(DD, BT, WW) hipLaunchKernelGGL((attn_bf16_kernel<DD, BT, WW>), grid, block, 0, stream, a)
+    if (W == 8) {
+      if (a.g.D == 128) { if (big_t) SA_LAUNCH_ATTN(128, true, 8); else SA_LAUNCH_ATTN(128, false, 8); }
+      else { if (big_t) SA_LAUNCH_ATTN(64, true, 8); else SA_LAUNCH_ATTN(64, false, 8); }
     } else {
-      if (big_t) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, dim3(256), 0, stream, a);
+      if (a.g.D == 128) { if (big_t) SA_LAUNCH_ATTN(128, true, 4); else SA_LAUNCH_ATTN(128, false, 4); }
+      else { if (big_t) SA_LAUNCH_ATTN(64, true, 4); else SA_LAUNCH_ATTN(64, false, 4); }
     }
+#undef SA_LAUNCH_ATTN
   } else {
     const dim3 grid((Lq + kF32Rows - 1) / kF32Rows, BH, 1);
     if (a.g.D == 128)
