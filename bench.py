@@ -81,29 +81,42 @@ def cpu_baseline(w, budget_s: float):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     T = w.tokens_per_frame
-    f = 20
-    res = ocache.resident_frames(f + 1, w.n_sink, w.n_local)
     bases = orope.theta_hat(w.theta0, w.sigma, np.zeros(w.n_heads))
-    kf, vf = [], []
-    for r in res:
-        kf.append(wl.frame_qkv(w, r, tensor=wl.TENSOR_K))
-        vf.append(wl.frame_qkv(w, r, tensor=wl.TENSOR_V))
-    q = wl.frame_qkv(w, f, tensor=wl.TENSOR_Q)
-    t0 = time.perf_counter()
-    # append: rotate the new frame's keys; attend: rotate q, attention head by head
-    kf_rot = [orope.rope3d_frame(k, r, bases, w.dims, w.grid[1]) for k, r in zip(kf, res)]
-    q_rot = orope.rope3d_frame(q, f, bases, w.dims, w.grid[1])
-    heads_done = 0
-    for h in range(w.n_heads):
-        oattn.window_attention(q_rot, kf_rot, vf, res, [f], T, True, heads=[h])
-        heads_done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    flops = attn_flops(T, len(res) * T, heads_done, w.head_dim)
+    f0 = 20
+    # Steady-state frames f0, f0+1, ...: each rotates its new frame's keys
+    # (append) and its queries, then attends head by head, until the budget
+    # is spent (checked after every head).  Only oracle calls are on the
+    # clock; drawing the seeded inputs is not.
+    k_rot, v_raw = {}, {}
+    heads_done, f, dt = 0, f0, 0.0
+    while dt <= budget_s:
+        res = ocache.resident_frames(f + 1, w.n_sink, w.n_local)
+        new_k = {r: wl.frame_qkv(w, r, tensor=wl.TENSOR_K) for r in res if r not in k_rot}
+        for r in new_k:
+            v_raw[r] = wl.frame_qkv(w, r, tensor=wl.TENSOR_V)
+        q = wl.frame_qkv(w, f, tensor=wl.TENSOR_Q)
+        t0 = time.perf_counter()
+        for r, k in new_k.items():
+            k_rot[r] = orope.rope3d_frame(k, r, bases, w.dims, w.grid[1])
+        q_rot = orope.rope3d_frame(q, f, bases, w.dims, w.grid[1])
+        dt += time.perf_counter() - t0
+        for h in range(w.n_heads):
+            t0 = time.perf_counter()
+            oattn.window_attention(q_rot, [k_rot[r] for r in res], [v_raw[r] for r in res], res, [f], T, True,
+                                   heads=[h])
+            dt += time.perf_counter() - t0
+            heads_done += 1
+            if dt > budget_s:
+                break
+        for r in [r for r in k_rot if r not in res]:
+            del k_rot[r], v_raw[r]
+        f += 1
+    n_keys = (w.n_sink + w.n_local) * T
+    flops = attn_flops(T, n_keys, heads_done, w.head_dim)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one steady-state frame (1560 queries x 18720 keys), {heads_done} of {w.n_heads} heads, "
-                      f"fp64 numpy incl. RoPE of all 12 cached frames; {dt:.1f} s",
+            "sample": f"{heads_done} head-frames ({heads_done / w.n_heads:.2f} steady-state frames from frame {f0}, "
+                      f"1560 queries x {n_keys} keys each), fp64 numpy incl. the RoPE of every key and query frame "
+                      f"it used; {dt:.1f} s of oracle time (input drawing excluded)",
             "latent_frames_per_s_per_layer": (heads_done / w.n_heads) / dt}
 
 

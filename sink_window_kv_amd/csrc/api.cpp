@@ -354,7 +354,7 @@ sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q,
   a.ws = static_cast<float*>(workspace);
   a.store_bytes = static_cast<uint32_t>(sa_cache_store_bytes(&c->desc));
   a.n_waves = sa::attn_waves(c->desc.dtype, c->desc.batch, c->desc.n_heads, c->desc.head_dim,
-                             c->desc.tokens_per_frame, n_q);
+                             c->desc.tokens_per_frame, n_q, device_cus());
   const hipError_t e = sa::launch_window_attn(a, c->desc.dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();

@@ -70,7 +70,7 @@ hipError_t launch_read(const CacheGeom& g, int store_slot, void* k_out, void* v_
                        hipStream_t stream);
 
 // Waves per workgroup and number of key splits the attention launch uses.
-int attn_waves(int dtype, int B, int H, int D, int T, int n_q);
+int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus);
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus);
 size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits);
 hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream);

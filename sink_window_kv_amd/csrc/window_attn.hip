@@ -152,8 +152,9 @@ __device__ __forceinline__ u32x4 lds_read(const StageSmem<D>& st, uint32_t byte_
 
 // BIG_T: every 64-key tile spans at most two frames (T >= 64), so frame and
 // slot are resolved once per tile with uniform arithmetic.
-// W waves per workgroup (W * 32 query rows).  W = 4: two workgroups per CU;
-// W = 8: one workgroup per CU, half the K/V traffic per query row.
+// W waves per workgroup (W * 32 query rows).  W = 4: two workgroups per CU,
+// two K/V stages each; W = 8: one workgroup per CU, three K/V stages, half
+// the K/V traffic per query row.
 template <int D, bool BIG_T, int W>
 __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   constexpr int kWaves = W;
@@ -371,21 +372,51 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
             as_bf16x8(lds_read(st, vaddr[q] + db * 32 * 8 * 16)), as_bf16x8(pk[q >> 1][q & 1]), oacc[db], 0, 0, 0);
   };
 
-  // ---- two-stage pipeline, unrolled by two so both stages are fixed
-  // objects: wait for tile kt, barrier (which also retires the stage read at
-  // kt-1), issue tile kt+1 into that stage, compute tile kt.
-  if (tile_lo < tile_hi) issue_tile(tile_lo, st0);
-  for (int kt = tile_lo; kt < tile_hi; kt += 2) {
-    wait_vmcnt0();
-    barrier();
-    if (kt + 1 < tile_hi) issue_tile(kt + 1, st1);
-    compute(kt, st0);
-    if (kt + 1 < tile_hi) {
+  if constexpr (W == 4) {
+    // ---- two stages (two workgroups share a CU's LDS), unrolled by two so
+    // both stages are fixed objects: wait for tile kt, barrier (which also
+    // retires the stage read at kt-1), issue tile kt+1 into that stage,
+    // compute tile kt.
+    if (tile_lo < tile_hi) issue_tile(tile_lo, st0);
+    for (int kt = tile_lo; kt < tile_hi; kt += 2) {
       wait_vmcnt0();
       barrier();
-      if (kt + 2 < tile_hi) issue_tile(kt + 2, st0);
-      compute(kt + 1, st1);
+      if (kt + 1 < tile_hi) issue_tile(kt + 1, st1);
+      compute(kt, st0);
+      if (kt + 1 < tile_hi) {
+        wait_vmcnt0();
+        barrier();
+        if (kt + 2 < tile_hi) issue_tile(kt + 2, st0);
+        compute(kt + 1, st1);
+      }
     }
+  } else {
+    // ---- three stages, two tiles in flight (one workgroup per CU).  Each
+    // step waits until only the newer tile's loads are outstanding, so tile
+    // kt has landed in every wave's share; the barrier also retires the
+    // stage that tile kt-1 was read from, which then receives tile kt+2.
+    // Past the end the last tile is fetched again into a stage nobody reads,
+    // which keeps the outstanding-load count the same in every step.
+    __shared__ StageSmem<D> st2;
+    const int t_last = tile_hi - 1;
+    if (tile_lo < tile_hi) {
+      issue_tile(tile_lo, st0);
+      issue_tile(min(tile_lo + 1, t_last), st1);
+    }
+    auto step = [&](int kt, const StageSmem<D>& cur, StageSmem<D>& nxt2) {
+      static_assert(KI + VI == 4 || KI + VI == 2, "one tile's DMA count per wave");
+      if constexpr (KI + VI == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      barrier();
+      issue_tile(min(kt + 2, t_last), nxt2);
+      compute(kt, cur);
+    };
+    for (int kt = tile_lo; kt < tile_hi; kt += 3) {
+      step(kt, st0, st2);
+      if (kt + 1 < tile_hi) step(kt + 1, st1, st0);
+      if (kt + 2 < tile_hi) step(kt + 2, st2, st1);
+    }
+    wait_vmcnt0();
   }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32db + 8(i/4) + 4hh + i%4.
@@ -561,18 +592,26 @@ __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int attn_waves(int dtype, int B, int H, int D, int T, int n_q) {
-  (void)B; (void)H; (void)D; (void)T; (void)n_q;
+int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus) {
+  (void)D;
   if (dtype != kBF16) return 1;
   if (const char* env = std::getenv("SA_ATTN_WAVES")) {
-    if (std::atoi(env) == 4) return 4;
+    const int v = std::atoi(env);
+    if (v == 4 || v == 8) return v;
   }
-  return 8;
+  // Eight waves (256 query rows, three K/V stages, one workgroup per CU)
+  // halve the K/V traffic per query row and keep two tiles in flight; that
+  // wins while the grid is about one round of CUs (one frame of one stream).
+  // Once the 128-row tiles alone cover the CUs several times over (batched
+  // streams, multi-frame chunks), two 4-wave workgroups per CU hide each
+  // other's barriers and win instead.
+  const int64_t tiles4 = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + 127) / 128);
+  return tiles4 >= 4LL * num_cus ? 4 : 8;
 }
 
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus) {
   if (dtype != kBF16) return 1;
-  const int W = attn_waves(dtype, B, H, D, T, n_q);
+  const int W = attn_waves(dtype, B, H, D, T, n_q, num_cus);
   const int64_t q_tile = 32LL * W;
   const int64_t tiles = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + q_tile - 1) / q_tile);
   const int64_t key_tiles = (static_cast<int64_t>(n_res) * T + kKTile - 1) / kKTile;

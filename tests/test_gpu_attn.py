@@ -4,6 +4,7 @@ bf16: rel-L2 <= 5e-3 and max-abs <= 2e-2; fp32: <= 1e-5.  At the Wan-1.3B
 shapes the oracle evaluates sampled query rows (every frame's first/last
 rows, tile edges, the ragged tail and random rows) over the full key set.
 """
+import contextlib
 import os
 
 import numpy as np
@@ -22,6 +23,25 @@ pytestmark = pytest.mark.gpu
 def _swk():
     import sink_window_kv_amd as swk
     return swk
+
+
+@contextlib.contextmanager
+def _env(**kv):
+    """Set launch-shape overrides (SA_ATTN_SPLITS, SA_ATTN_WAVES) for the block; None leaves one unset."""
+    old = {k: os.environ.get(k) for k in kv}
+    for k, v in kv.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 class GpuStream:
@@ -80,29 +100,21 @@ def test_cfg1_tiny_f32_stream():
             _check(gs, q, o, mask == swk.SA_MASK_FRAME_CAUSAL, what=f"cfg1 frame {f} mask {mask}")
 
 
-@pytest.mark.parametrize("splits", [None, "1", "5"])
-def test_cfg2_wan_layer_stream(splits):
+@pytest.mark.parametrize("splits,waves", [(None, None), ("1", None), ("5", None), (None, "4"), ("3", "4")])
+def test_cfg2_wan_layer_stream(splits, waves):
     """Wan-1.3B layer, bf16, 3 sink + 9 local, 40 frames; checks while filling and in steady state."""
     swk = _swk()
     w = wl.WORKLOADS[2]
-    old = os.environ.get("SA_ATTN_SPLITS")
-    if splits is not None:
-        os.environ["SA_ATTN_SPLITS"] = splits
-    try:
+    with _env(SA_ATTN_SPLITS=splits, SA_ATTN_WAVES=waves):
         gs = GpuStream(w)
         rows = sample_rows(w.tokens_per_frame, w.tokens_per_frame)
-        check = {0, 1, 2, 3, 11, 12, 20, 39} if splits is None else {2, 13, 39}
+        check = {0, 1, 2, 3, 11, 12, 20, 39} if splits is None and waves is None else {2, 13, 39}
         for f in range(w.frames):
             q, k, v = (wl.frame_qkv(w, f, tensor=t) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
             gs.append(k, v, 1, f)
             if f in check:
                 o = gs.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
-                _check(gs, q, o, True, rows=rows, what=f"cfg2 frame {f} splits {splits}")
-    finally:
-        if old is None:
-            os.environ.pop("SA_ATTN_SPLITS", None)
-        else:
-            os.environ["SA_ATTN_SPLITS"] = old
+                _check(gs, q, o, True, rows=rows, what=f"cfg2 frame {f} splits {splits} waves {waves}")
 
 
 def test_cfg2_unscaled_scores_and_custom_scale():
@@ -168,7 +180,8 @@ def test_cfg3_lol_jitter_long_positions():
             log(f"  rel_l2 {rel:.2e} max_abs {mx:.2e}")
 
 
-def test_cfg5_chunked_causal_batched():
+@pytest.mark.parametrize("waves", [None, "8"])
+def test_cfg5_chunked_causal_batched(waves):
     """B = 4 streams, 3-frame query chunks, frame-causal inside the chunk, sigma = 0.8 (layer 29 seeds)."""
     swk = _swk()
     w = wl.WORKLOADS[5]
@@ -185,9 +198,10 @@ def test_cfg5_chunked_causal_batched():
         k = wl.chunk_qkv(w, f0, w.chunk, layer, wl.TENSOR_K)
         v = wl.chunk_qkv(w, f0, w.chunk, layer, wl.TENSOR_V)
         gs.append(k, v, w.chunk, f0)
-        if c in (0, 1, 3, 9):
-            o = gs.attend(q, w.chunk, swk.SA_MASK_FRAME_CAUSAL)
-            _check(gs, q, o, True, rows=rows, heads=heads, what=f"cfg5 chunk {c}")
+        if c in ((0, 1, 3, 9) if waves is None else (3, 9)):
+            with _env(SA_ATTN_WAVES=waves):
+                o = gs.attend(q, w.chunk, swk.SA_MASK_FRAME_CAUSAL)
+            _check(gs, q, o, True, rows=rows, heads=heads, what=f"cfg5 chunk {c} waves {waves}")
 
 
 @pytest.mark.parametrize("D,dims,grid,n_sink,n_local,n_q,mask,frames", [
@@ -196,7 +210,8 @@ def test_cfg5_chunked_causal_batched():
     (128, (44, 42, 42), (1, 8), 0, 64, 1, 1, 80),  # the largest window (64 frames), no sinks
     (128, (44, 42, 42), (5, 40), 3, 9, 1, 1, 14),  # T = 200: key tiles straddle frames
 ])
-def test_small_shapes_bf16(D, dims, grid, n_sink, n_local, n_q, mask, frames):
+@pytest.mark.parametrize("waves", ["4", "8"])
+def test_small_shapes_bf16(D, dims, grid, n_sink, n_local, n_q, mask, frames, waves):
     w = wl.Workload("edge", 42, batch=2, n_heads=3, head_dim=D, dims=dims, grid=grid, n_sink=n_sink,
                     n_local=n_local, chunk=n_q, frames=frames, dtype="bf16", sigma=0.8)
     eps = wl.head_jitter(w)
@@ -208,8 +223,9 @@ def test_small_shapes_bf16(D, dims, grid, n_sink, n_local, n_q, mask, frames):
         k = wl.chunk_qkv(w, f, n_q, 0, wl.TENSOR_K)
         v = wl.chunk_qkv(w, f, n_q, 0, wl.TENSOR_V)
         gs.append(k, v, n_q, 3 * f + 1)
-        o = gs.attend(q, n_q, mask)
-        _check(gs, q, o, mask == 1, what=f"edge D={D} T={T} frame {f}")
+        with _env(SA_ATTN_WAVES=waves):
+            o = gs.attend(q, n_q, mask)
+        _check(gs, q, o, mask == 1, what=f"edge D={D} T={T} frame {f} waves {waves}")
         f += n_q
 
 
