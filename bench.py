@@ -45,7 +45,22 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy three times (HBM counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A copy kernel of known size: reads and writes 512 MiB per launch.  Its
+    FETCH_SIZE / WRITE_SIZE counters give the scale from counter KiB to HBM bytes."""
+    import torch
+    n = 128 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": 4 * n, "copy_bytes_written_per_launch": 4 * n}), flush=True)
 
 
 def traffic_from_profile(kernel_src: str):
@@ -122,6 +137,9 @@ def cpu_baseline(w, budget_s: float):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
