@@ -251,6 +251,49 @@ def main():
     rc_flops = 2.0 * (n_win * T) * (2 * H * D) * w4.hidden
     rc_bytes = (n_win * T * w4.hidden + 2 * H * D * w4.hidden + 2 * n_win * T * H * D) * 2
 
+    # Chunked, batched shape: B = 4 streams, 3-frame query chunks, frame-causal
+    # (4680 queries per stream over 10/11/12 visible frames), sigma = 0.8.
+    w5 = wl.WORKLOADS[5]
+    eps5 = wl.head_jitter(w5, layer=0)
+    rope5 = swk.Rope(H, D, w5.dims, w5.grid, w5.theta0, w5.sigma, eps5)
+    c5 = swk.Cache(rope5, w5.batch, w5.n_sink, w5.n_local, bf, device=dev)
+    chunks5 = []
+    for ci in range(4):
+        f0 = ci * w5.chunk
+        chunks5.append(tuple(torch.from_numpy(wl.chunk_qkv(w5, f0, w5.chunk, 0, t)).to(dev, bf).contiguous()
+                             for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V)))
+    t5 = 0
+    for ci in range(4):  # fill: 12 frames resident after four chunks
+        swk.sa_cache_append(c5, chunks5[ci][1], chunks5[ci][2], w5.chunk, t5)
+        t5 += w5.chunk
+    ws5_bytes = swk.sa_window_attn_workspace(c5, w5.chunk)
+    ws5 = torch.zeros(max(ws5_bytes // 4, 4), dtype=torch.float32, device=dev)
+    o5 = torch.empty_like(chunks5[0][0])
+    a5_ms, ap5_ms = [], []
+    for it in range(13):
+        q5, k5, v5 = chunks5[it % 4]
+        ea, eb, ec = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ea.record(stream)
+        swk.sa_cache_append(c5, k5, v5, w5.chunk, t5)
+        eb.record(stream)
+        swk.sa_window_attn(c5, q5, o5, w5.chunk, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws5)
+        ec.record(stream)
+        t5 += w5.chunk
+        torch.cuda.synchronize()
+        if it >= 3:
+            ap5_ms.append(ea.elapsed_time(eb))
+            a5_ms.append(eb.elapsed_time(ec))
+    # visible keys per query frame i of the chunk: 3 sinks + (7 + i) local frames
+    flops5 = sum(attn_flops(T, (w5.n_sink + w5.n_local - (w5.chunk - 1) + i) * T, H, D)
+                 for i in range(w5.chunk)) * w5.batch
+    a5_avg = sum(a5_ms) / len(a5_ms)
+    ap5_avg = sum(ap5_ms) / len(ap5_ms)
+    print(f"[bench] B=4 3-frame chunks: attention {a5_avg * 1e3:.1f} us "
+          f"({flops5 / (a5_avg * 1e-3) / 1e12:.0f} TFLOP/s), append {ap5_avg * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    c5.close()
+    rope5.close()
+
     traffic = traffic_from_profile(os.path.join(ROOT, "sink_window_kv_amd", "csrc", "window_attn.hip"))
     out = {
         "metric": "sink+window attn TFLOP/s & latent frames/s/layer on 1 MI355X; % bf16 MFMA peak",
@@ -286,6 +329,13 @@ def main():
                     "TFLOPs": round(rc_flops / (rc_us * 1e-6) / 1e12, 1),
                     "pct_bf16_peak": round(100.0 * rc_flops / (rc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
                     "min_bytes": rc_bytes},
+        "chunked_b4": {"workload": "wan13b-chunk3-b4: B=4, 3-frame query chunks (4680 queries per stream), "
+                                    "frame-causal over 10/11/12 visible frames, sigma=0.8, one layer",
+                       "attention_avg_us": round(a5_avg * 1e3, 1), "flops": flops5,
+                       "TFLOPs": round(flops5 / (a5_avg * 1e-3) / 1e12, 1),
+                       "pct_bf16_peak": round(100.0 * flops5 / (a5_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                       "append_avg_us": round(ap5_avg * 1e3, 1),
+                       "latent_frames_per_s_per_layer": round(w5.batch * w5.chunk / ((a5_avg + ap5_avg) * 1e-3), 1)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

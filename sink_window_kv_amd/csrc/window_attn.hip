@@ -9,10 +9,11 @@
 // increasing frame order, every query row sees a prefix [0, kend) of the
 // logical key sequence.
 //
-// bf16 kernel (gfx950 matrix cores).  A workgroup of 4 waves owns 128 query
-// rows of one (stream, head); two workgroups share a CU, so each SIMD runs
-// two waves from different workgroups and one wave's softmax overlaps the
-// other's matrix-core work.
+// bf16 kernel (gfx950 matrix cores).  A workgroup of W waves owns 32 W query
+// rows of one (stream, head), and each SIMD runs two waves, so one wave's
+// softmax overlaps the other's matrix-core work.  W = 8 (one workgroup per
+// CU, three K/V stages, two tiles in flight) for grids of about one round of
+// CUs; W = 4 (two workgroups per CU, two stages each) for large grids.
 //   * Each wave owns 32 query rows and computes S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16, so that every lane holds the scores of ONE
 //     query (column) for 16 keys per 32-key block: the row max and row sum are
@@ -27,7 +28,7 @@
 //   * Online softmax in the exp2 domain with a lazily raised running max; the
 //     row sum is accumulated from the same bf16-rounded p the PV product uses.
 //   * K and V^T tiles of 64 keys go global -> LDS by direct-to-LDS buffer
-//     loads into two XOR-swizzled stages (no VGPR staging, conflict-free
+//     loads into XOR-swizzled stages (no VGPR staging, conflict-free
 //     operand reads); per-tile frame bases come from the slot table, so sink
 //     and ring frames are read in place with no gather copy.
 // For one stream at Wan-1.3B shapes the (q-tile, head) grid alone does not
