@@ -189,11 +189,10 @@ sa_status sa_window_attn_workspace(const sa_cache* cache, int32_t n_q, size_t* b
  *         frames (append first, then attend); q is rotated at those frames' t.
  *   scale 0 => 1/sqrt(D).
  *   workspace: device scratch of at least sa_window_attn_workspace() bytes
- *         (NULL allowed when that is 0); SA_ERR_RANGE if too small.  It must
- *         be zero-filled before its first use; every call leaves its first
- *         4096 bytes (arrival counters) zero again, so one workspace serves
- *         any number of calls and shapes.  Calls sharing a workspace must not
- *         run concurrently (stream order is enough).
+ *         (NULL allowed when that is 0); SA_ERR_RANGE if too small.  It holds
+ *         the key-split partial results of this call only and needs no
+ *         initialisation.  Calls sharing a workspace must not run
+ *         concurrently (stream order is enough).
  * o must not alias q. */
 sa_status sa_window_attn(const sa_cache* cache, const void* q, void* o, int32_t n_q, float scale,
                          sa_mask mask, void* workspace, size_t workspace_bytes, void* stream);

@@ -32,9 +32,11 @@
 //     operand reads); per-tile frame bases come from the slot table, so sink
 //     and ring frames are read in place with no gather copy.
 // For one stream at Wan-1.3B shapes the (q-tile, head) grid alone does not
-// fill 256 CUs, so the key range is split; each split publishes a partial
-// (O, m, l) and the last split of a q-tile to arrive (atomic counter) merges
-// them in split order (deterministic) -- one kernel per call.
+// fill 256 CUs, so the key range is split; each split writes a partial
+// (O, m, l) and a small second kernel merges them in split order
+// (deterministic).  The kernel boundary orders the two: a merge inside the
+// attention kernel would need device-scope fences, which on this chip write
+// back and invalidate whole L2 slices and cost more than the merge itself.
 //
 // fp32 kernel: one thread per query row, VALU FMA, for the small fp32
 // configurations (accuracy 1e-5 against an fp64 reference).
@@ -60,12 +62,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // score exceeds it by more than this (log2 units), so p <= 2^kLazy.
 constexpr float kLazy = 8.f;
 
-// Workspace layout (float units): [0, 1024) int32 arrival counters, one per
-// (stream, head, q-tile); then split partials O [S][B][H][Lq][D] (fp32,
-// unnormalised) and (m, l) [S][B][H][Lq][2].  The counters must be zero
-// before the first call; the last-arriving workgroup of a tile resets its
-// counter, so every call leaves them zero again.
-constexpr int kMaxTileCounters = 1024;
+// Workspace layout (float units): split partials O [S][B][H][Lq][D] (fp32,
+// unnormalised), then (m, l) [S][B][H][Lq][2].  Every call writes all of it
+// before reading it, so it needs no initialisation.
 
 __device__ __forceinline__ int key_perm(int m) {  // swap bits 2 and 3
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -162,7 +161,6 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   constexpr int kQTile = W * kQW;  // query rows per workgroup
   __shared__ StageSmem<D> st0, st1;
   __shared__ int s_slot[kMaxFrames];
-  __shared__ int s_last;
   constexpr int CPR = D / 8;                      // K chunks per key row
   constexpr int KI = kKTile * CPR / 64 / kWaves;  // K DMA instructions per wave per tile
   constexpr int VI = D * 8 / 64 / kWaves;         // V^T DMA instructions per wave per tile
@@ -340,7 +338,7 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
     }
     float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+    for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, sacc[0][i]), sacc[1][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
@@ -421,17 +419,13 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32db + 8(i/4) + 4hh + i%4.
-  float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (a.n_splits > 1) {
-    // Publish this split's partial, then the last-arriving split of the
-    // q-tile merges all of them (fixed split order, so results are
-    // deterministic) and writes O.
-    const int64_t plane = static_cast<int64_t>(g.B) * g.H * Lq;
-    float* part_o = a.ws + kMaxTileCounters;
-    float* part_ml = part_o + static_cast<int64_t>(a.n_splits) * plane * D;
-    const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
+    // Publish this split's partial; attn_merge_kernel combines the splits.
     if (row_ok) {
-      float* po = part_o + (split * plane + prow) * D;
+      const int64_t plane = static_cast<int64_t>(g.B) * g.H * Lq;
+      const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
+      float* po = a.ws + (split * plane + prow) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -440,45 +434,12 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
           *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
         }
       if (hh == 0) {
-        part_ml[(split * plane + prow) * 2] = m_run;
-        part_ml[(split * plane + prow) * 2 + 1] = l_tot;
+        float* pml = a.ws + static_cast<int64_t>(a.n_splits) * plane * D + (split * plane + prow) * 2;
+        pml[0] = m_run;
+        pml[1] = l_tot;
       }
     }
-    __threadfence();
-    __syncthreads();
-    int* counters = reinterpret_cast<int*>(a.ws);
-    const int tile_id = bh * n_qt + qt;
-    if (threadIdx.x == 0) {
-      const int prev = atomicAdd(&counters[tile_id], 1);
-      s_last = prev == a.n_splits - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (threadIdx.x == 0) atomicExch(&counters[tile_id], 0);
-    if (!row_ok) return;
-    float M = kNegInf;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]));
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    l_tot = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-      const float ms = __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2]);
-      if (ms == kNegInf) continue;
-      const float w = __builtin_amdgcn_exp2f(ms - M);
-      l_tot += __builtin_nontemporal_load(&part_ml[(s * plane + prow) * 2 + 1]) * w;
-      const float* po = part_o + (s * plane + prow) * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(po + 32 * db + 8 * gq + 4 * hh));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[db][4 * gq + i] += x[i] * w;
-        }
-    }
+    return;
   }
   if (row_ok) {
     const float inv = 1.f / l_tot;
@@ -498,6 +459,45 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
 // fp32 path: one thread per query row, 32-key tiles staged in LDS.
 constexpr int kF32Rows = 64;
 constexpr int kF32Keys = 32;
+
+// Split merge: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s, splits in order.  16 lanes per row, 8 channels each.
+template <int D>
+__global__ void __launch_bounds__(256) attn_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
+                                                         int B, int H, int Lq, int n_splits) {
+  constexpr int kLanes = D / 8;
+  constexpr int kRows = 256 / kLanes;
+  const int64_t plane = static_cast<int64_t>(B) * H * Lq;
+  const int64_t prow = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / kLanes;  // (b*H + h)*Lq + row
+  const int c8 = (threadIdx.x % kLanes) * 8;
+  if (prow >= plane) return;
+  const float* pml = ws + static_cast<int64_t>(n_splits) * plane * D;
+  float M = kNegInf;
+  for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, pml[(sp * plane + prow) * 2]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float ms = pml[(sp * plane + prow) * 2];
+    if (ms == kNegInf) continue;
+    const float w = __builtin_amdgcn_exp2f(ms - M);
+    l += pml[(sp * plane + prow) * 2 + 1] * w;
+    const f32x4* src = reinterpret_cast<const f32x4*>(ws + (sp * plane + prow) * D + c8);
+    const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += x0[i] * w;
+      acc[4 + i] += x1[i] * w;
+    }
+  }
+  const float inv = 1.f / l;
+  const int64_t bh = prow / Lq;
+  const int row = static_cast<int>(prow - bh * Lq);
+  const int b = static_cast<int>(bh / H), h = static_cast<int>(bh - static_cast<int64_t>(b) * H);
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = cvt_pk_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *reinterpret_cast<u32x4*>(o + ((static_cast<int64_t>(b) * Lq + row) * H + h) * D + c8) = out;
+}
 
 template <int D>
 __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
@@ -616,7 +616,6 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
   const int64_t q_tile = 32LL * W;
   const int64_t tiles = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + q_tile - 1) / q_tile);
   const int64_t key_tiles = (static_cast<int64_t>(n_res) * T + kKTile - 1) / kKTile;
-  if (tiles > kMaxTileCounters) return 1;
   int64_t max_s = key_tiles / 8;  // at least 8 key tiles per split
   if (max_s > 16) max_s = 16;
   if (max_s < 1) max_s = 1;
@@ -645,7 +644,7 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
 size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits) {
   if (dtype != kBF16 || n_splits <= 1) return 0;
   const size_t rows = static_cast<size_t>(B) * H * n_q * T;
-  return (static_cast<size_t>(kMaxTileCounters) + static_cast<size_t>(n_splits) * rows * (D + 2)) * sizeof(float);
+  return static_cast<size_t>(n_splits) * rows * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) {
@@ -666,6 +665,19 @@ hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) 
       else { if (big_t) SA_LAUNCH_ATTN(64, true, 4); else SA_LAUNCH_ATTN(64, false, 4); }
     }
 #undef SA_LAUNCH_ATTN
+    if (a.n_splits > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t rows = static_cast<int64_t>(a.g.B) * a.g.H * Lq;
+      const int rows_per_block = 256 / (a.g.D / 8);
+      const dim3 mgrid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+      if (a.g.D == 128)
+        hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, dim3(256), 0, stream, a.ws, static_cast<uint16_t*>(a.o),
+                           a.g.B, a.g.H, Lq, a.n_splits);
+      else
+        hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, dim3(256), 0, stream, a.ws, static_cast<uint16_t*>(a.o),
+                           a.g.B, a.g.H, Lq, a.n_splits);
+    }
   } else {
     const dim3 grid((Lq + kF32Rows - 1) / kF32Rows, BH, 1);
     if (a.g.D == 128)
