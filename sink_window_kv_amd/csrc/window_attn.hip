@@ -84,6 +84,31 @@ __device__ __forceinline__ float dot2_ones(uint32_t pk, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
 }
 
+// max(x, x of the lane 32 apart): the two half-waves swap their copies with
+// v_permlane32_swap (a VALU op, no LDS round trip).  The s_nop covers the
+// VALU-write -> permlane-read hazard on the operands.
+__device__ __forceinline__ float max_halves(float x) {
+  float lo = x, hi = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+  return fmaxf(lo, hi);
+}
+
+// Max of the 32 scores a lane holds for one 64-key tile, as a shallow tree
+// of three-input maxima (a dependent chain would be 16 deep).
+__device__ __forceinline__ float tile_max(const mfma_f32x16 (&s)[2]) {
+  float a[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int j = 3 * i;
+    const float x0 = s[j >> 4][j & 15], x1 = s[(j + 1) >> 4][(j + 1) & 15], x2 = s[(j + 2) >> 4][(j + 2) & 15];
+    a[i] = fmaxf(fmaxf(x0, x1), x2);
+  }
+  a[10] = fmaxf(s[1][14], s[1][15]);
+  const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
+  return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+}
+
 // Raw buffer descriptor (gfx9 layout) over [base, base + bytes), in SGPRs.
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
@@ -191,7 +216,7 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   const bool row_ok = row < Lq;
   const int qf = row_ok ? row / T : a.n_q - 1;
   const int kend = a.causal ? (first_q + qf + 1) * T : n_keys;
-  const int wave_row0 = qt * kQTile + wave * kQW;
+  const int wave_row0 = qt * kQTile + wave_u * kQW;  // wave-uniform (scalar) from here on
   const bool wave_active = wave_row0 < Lq;
   const int wave_last = min(wave_row0 + kQW - 1, Lq - 1);
   const int wave_kend = a.causal ? (first_q + wave_last / T + 1) * T : n_keys;            // largest kend
@@ -260,15 +285,37 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   // landing at chunk (base + L); the lane fetches whichever global chunk the
   // swizzled layout puts there.  Keys past kend_wg are clamped to the tile's
   // first key (resident, finite): their scores are masked, they add nothing.
-  auto issue_tile = [&](int kt, StageSmem<D>& st) {
+  // plan_tile resolves a tile's frames and this lane's byte offsets; fire
+  // issues one of the wave's KI + VI transfers.  The transfers of the next
+  // tiles are spread over the current tile's S^T products: issued together
+  // they queue at the CU's texture addresser and stall every wave.
+  struct TilePlan {
+    uint32_t off[KI + VI];
+  };
+  // Frame of the tiles being planned (BIG_T): tiles are planned in
+  // non-decreasing order, so the frame lf0 of a tile's first key and the
+  // store offsets of frames lf0 and lf0+1 are advanced, not recomputed.
+  int pl_lf0 = 0, pl_jb = T;
+  uint32_t pl_b0 = 0, pl_b1 = 0;
+  if (BIG_T) {
+    pl_b0 = blk_bytes(0);
+    pl_b1 = blk_bytes(min(1, n_res - 1));
+  }
+  auto plan_tile = [&](int kt) {
+    TilePlan p;
     const int j0 = kt * kKTile;
     uint32_t koff0 = 0, koff1 = 0, voff0 = 0, voff1 = 0;
     int jb = 0;
     if (BIG_T) {
-      const int lf0 = j0 / T;
-      jb = (lf0 + 1) * T;
-      const int lf1 = min(lf0 + 1, n_res - 1);
-      const uint32_t b0 = blk_bytes(lf0), b1 = blk_bytes(lf1);
+      while (j0 >= pl_jb) {
+        ++pl_lf0;
+        pl_jb += T;
+        pl_b0 = pl_b1;
+        pl_b1 = blk_bytes(min(pl_lf0 + 1, n_res - 1));
+      }
+      const int lf0 = pl_lf0;
+      jb = pl_jb;
+      const uint32_t b0 = pl_b0, b1 = pl_b1;
       koff0 = b0 - static_cast<uint32_t>(lf0) * blk_elems * 2;
       koff1 = b1 - static_cast<uint32_t>(jb) * D * 2;
       voff0 = b0 - static_cast<uint32_t>(lf0) * T * 2;
@@ -276,8 +323,7 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < KI; ++u) {
-      const int i = wave_u * KI + u;
-      const int P = 64 * i + lane;
+      const int P = 64 * (wave_u * KI + u) + lane;
       const int r = P / CPR, c = (P % CPR) ^ kswz<D>(r);
       int j = j0 + r;
       if (j >= kend_wg) j = j0;
@@ -289,12 +335,11 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
         off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
               static_cast<uint32_t>(j - lf * T) * (D * 2);
       }
-      dma16(krsrc, off + c * 16, &st.k[64 * i]);
+      p.off[u] = off + c * 16;
     }
 #pragma unroll
     for (int u = 0; u < VI; ++u) {
-      const int i = wave_u * VI + u;
-      const int P = 64 * i + lane;
+      const int P = 64 * (wave_u * VI + u) + lane;
       const int d = P / 8, c = (P % 8) ^ vswz(d);
       int j = j0 + c * 8;
       if (j >= kend_wg) j = j0;
@@ -306,27 +351,52 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
         off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
               static_cast<uint32_t>(d) * T * 2 + static_cast<uint32_t>(j - lf * T) * 2;
       }
-      dma16(vrsrc, off, &st.vt[64 * i]);
+      p.off[KI + u] = off;
     }
+    return p;
   };
+  auto fire = [&](const TilePlan& p, int u, StageSmem<D>& st) {
+    if (u < KI)
+      dma16(krsrc, p.off[u], &st.k[64 * (wave_u * KI + u)]);
+    else
+      dma16(vrsrc, p.off[u], &st.vt[64 * (wave_u * VI + (u - KI))]);
+  };
+  auto issue_tile = [&](int kt, StageSmem<D>& st) {
+    const TilePlan p = plan_tile(kt);
+#pragma unroll
+    for (int u = 0; u < KI + VI; ++u) fire(p, u, st);
+  };
+  // one transfer after every kFireStep pairs of S^T products
+  constexpr int kFireStep = (D / 16) / (KI + VI) > 0 ? (D / 16) / (KI + VI) : 1;
+  static_assert((D / 16) / kFireStep >= KI + VI, "every transfer has a slot in the S^T loop");
 
   // ---- one 64-key tile: S^T for both 32-key blocks (two independent
   // accumulation chains), softmax of the 32 scores each lane holds, then
   // O^T += V^T P^T over four channel blocks.
-  auto compute = [&](int kt, const StageSmem<D>& st) {
+  // With do_fire, the wave's transfers of plan np into stage nst are issued
+  // in between (or, for a wave with nothing to compute, at once).
+  auto compute = [&](int kt, const StageSmem<D>& st, bool do_fire, const TilePlan& np, StageSmem<D>& nst) {
     const int j0 = kt * kKTile;
-    if (!wave_active || j0 >= wave_kend) return;
+    if (!wave_active || j0 >= wave_kend) {
+      if (do_fire) {
+#pragma unroll
+        for (int u = 0; u < KI + VI; ++u) fire(np, u, nst);
+      }
+      return;
+    }
     mfma_f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
+    for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read(st, kaddr[s] + kb * 32 * CPR * 16)),
                                                             qfrag[s], sacc[kb], 0, 0, 0);
+      if (do_fire && s % kFireStep == 0 && s / kFireStep < KI + VI) fire(np, s / kFireStep, nst);
+    }
     // mask (register i of block kb holds key j0 + 32kb + 16(i/8) + 8hh + i%8)
     if (j0 + kKTile > wave_kmin) {
       const int lim = kend - j0 - 8 * hh;  // keys j0 + 8hh + off with off >= lim are hidden
@@ -336,10 +406,7 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + 16 * (i >> 3) + (i & 7) >= lim) sacc[kb][i] = kNegInf;
     }
-    float mx = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, sacc[0][i]), sacc[1][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    const float mx = max_halves(tile_max(sacc)) * a.scale_log2;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -374,19 +441,17 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   if constexpr (W == 4) {
     // ---- two stages (two workgroups share a CU's LDS), unrolled by two so
     // both stages are fixed objects: wait for tile kt, barrier (which also
-    // retires the stage read at kt-1), issue tile kt+1 into that stage,
-    // compute tile kt.
+    // retires the stage read at kt-1), compute tile kt while issuing tile
+    // kt+1 into that stage.
     if (tile_lo < tile_hi) issue_tile(tile_lo, st0);
     for (int kt = tile_lo; kt < tile_hi; kt += 2) {
       wait_vmcnt0();
       barrier();
-      if (kt + 1 < tile_hi) issue_tile(kt + 1, st1);
-      compute(kt, st0);
+      compute(kt, st0, kt + 1 < tile_hi, plan_tile(min(kt + 1, tile_hi - 1)), st1);
       if (kt + 1 < tile_hi) {
         wait_vmcnt0();
         barrier();
-        if (kt + 2 < tile_hi) issue_tile(kt + 2, st0);
-        compute(kt + 1, st1);
+        compute(kt + 1, st1, kt + 2 < tile_hi, plan_tile(min(kt + 2, tile_hi - 1)), st0);
       }
     }
   } else {
@@ -407,8 +472,7 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
       if constexpr (KI + VI == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
       barrier();
-      issue_tile(min(kt + 2, t_last), nxt2);
-      compute(kt, cur);
+      compute(kt, cur, true, plan_tile(min(kt + 2, t_last)), nxt2);
     };
     for (int kt = tile_lo; kt < tile_hi; kt += 3) {
       step(kt, st0, st2);
