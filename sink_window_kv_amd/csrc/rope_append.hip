@@ -143,6 +143,78 @@ __global__ void __launch_bounds__(256) append_v_kernel(CacheGeom g, const E* __r
   }
 }
 
+// bf16 keys and values of a chunk in one pass: a workgroup owns 64 tokens
+// x 64 channels of one (frame, stream, head), so even one frame of one
+// stream spreads over a few hundred workgroups.  Every load is issued first
+// (16-byte vectors, 128-byte row pieces), then K is rotated and written into
+// [slot][b][h][tok][d] and V goes through LDS into [slot][b][h][d][tok]
+// (128-byte row pieces).  Store offsets are 32-bit (a store is below 4 GiB).
+template <int D>
+__global__ void __launch_bounds__(256) append_kv_bf16_kernel(RopeArgs rope, CacheGeom g,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v,
+                                                              FrameTable chunk) {
+  constexpr int VE = 8;                      // bf16 per 16-byte vector
+  constexpr int DW = 64;                     // channels per workgroup
+  constexpr int VPR = DW / VE;               // vectors per token row piece
+  constexpr int NV = kVTileTok * VPR / 256;  // vectors per thread (K and V each)
+  static_assert(NV * 256 == kVTileTok * VPR, "whole tile per workgroup");
+  __shared__ uint16_t tile[kVTileTok][DW + VE];
+  constexpr int parts = D / DW;
+  const int tok0 = (blockIdx.x / parts) * kVTileTok;
+  const int d0 = (blockIdx.x % parts) * DW;
+  const int h = blockIdx.y;
+  const int j = blockIdx.z % chunk.n;
+  const int b = blockIdx.z / chunk.n;
+  const int T = g.T;
+  const int64_t src0 = ((static_cast<int64_t>(b) * chunk.n + j) * T * g.H + h) * D + d0;
+  const uint64_t src_tok_stride = static_cast<uint64_t>(g.H) * D;
+  u32x4 kv[NV], vv[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int r = e / VPR, cv = e % VPR;
+    const int tok = min(tok0 + r, T - 1);
+    const uint64_t off = static_cast<uint64_t>(tok) * src_tok_stride + cv * VE;
+    kv[u] = *reinterpret_cast<const u32x4*>(k + src0 + off);
+    vv[u] = *reinterpret_cast<const u32x4*>(v + src0 + off);
+  }
+  const int slot = chunk.store_slot[j];
+  const uint32_t blk = ((static_cast<uint32_t>(slot) * g.B + b) * g.H + h) * static_cast<uint32_t>(T) * D;
+  uint16_t* kst = static_cast<uint16_t*>(g.k_store);
+  uint16_t* vst = static_cast<uint16_t*>(g.v_store);
+  const double* freq_h = rope.freq + static_cast<size_t>(h) * (D / 2);
+  const int64_t t = chunk.t[j];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int r = e / VPR, cv = e % VPR;
+    const int tok = tok0 + r;
+    *reinterpret_cast<u32x4*>(&tile[r][cv * VE]) = vv[u];
+    if (tok < T) {
+      float x[8];
+      unpack_bf16x8(kv[u], x);
+      rope_rotate8(rope, freq_h, d0 / 8 + cv, t, tok / rope.grid_w, tok % rope.grid_w, x);
+      *reinterpret_cast<u32x4*>(kst + blk + static_cast<uint32_t>(tok) * D + d0 + cv * VE) = pack_bf16x8(x);
+    }
+  }
+  __syncthreads();
+  constexpr int VPC = kVTileTok / VE;  // vectors per output row piece
+#pragma unroll
+  for (int u = 0; u < DW * VPC / 256; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int d = e / VPC, cv = e % VPC;
+    const int tok = tok0 + cv * VE;
+    if (tok < T) {
+      uint16_t vals[VE];
+#pragma unroll
+      for (int i = 0; i < VE; ++i) vals[i] = tile[cv * VE + i][d];
+      *reinterpret_cast<u32x4*>(vst + blk + static_cast<uint32_t>(d0 + d) * T + tok) =
+          *reinterpret_cast<const u32x4*>(vals);
+    }
+  }
+}
+
 // Copy one stored frame out in the boundary layout [B, T, H, D].
 template <typename E>
 __global__ void __launch_bounds__(256) read_kernel(CacheGeom g, int slot, E* __restrict__ k_out,
@@ -193,14 +265,13 @@ hipError_t launch_append(const RopeArgs& rope, const CacheGeom& g, const void* k
   const int64_t work = static_cast<int64_t>(g.B) * chunk.n * g.T * g.H * (g.D / 8);
   const dim3 vgrid((g.T + kVTileTok - 1) / kVTileTok, g.H, g.B * chunk.n);
   if (dtype == kBF16) {
-    hipLaunchKernelGGL(append_k_kernel<uint16_t>, dim3(grid_for(work)), dim3(256), 0, stream, rope,
-                       g, static_cast<const uint16_t*>(k), chunk);
+    const dim3 kvgrid(vgrid.x * (g.D / 64), vgrid.y, vgrid.z);
     if (g.D == 128)
-      hipLaunchKernelGGL((append_v_kernel<uint16_t, 128>), vgrid, dim3(256), 0, stream, g,
-                         static_cast<const uint16_t*>(v), chunk);
+      hipLaunchKernelGGL(append_kv_bf16_kernel<128>, kvgrid, dim3(256), 0, stream, rope, g,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk);
     else
-      hipLaunchKernelGGL((append_v_kernel<uint16_t, 64>), vgrid, dim3(256), 0, stream, g,
-                         static_cast<const uint16_t*>(v), chunk);
+      hipLaunchKernelGGL(append_kv_bf16_kernel<64>, kvgrid, dim3(256), 0, stream, rope, g,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk);
   } else {
     hipLaunchKernelGGL(append_k_kernel<float>, dim3(grid_for(work)), dim3(256), 0, stream, rope, g,
                        static_cast<const float*>(k), chunk);
