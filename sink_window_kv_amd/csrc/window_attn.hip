@@ -12,8 +12,8 @@
 // bf16 kernel (gfx950 matrix cores).  A workgroup of W waves owns 32 W query
 // rows of one (stream, head), and each SIMD runs two waves, so one wave's
 // softmax overlaps the other's matrix-core work.  W = 8 (one workgroup per
-// CU, three K/V stages, two tiles in flight) for grids of about one round of
-// CUs; W = 4 (two workgroups per CU, two stages each) for large grids.
+// CU, three K/V stages, two tiles in flight) by default; W = 4 (two
+// workgroups per CU, two stages each) on request.
 //   * Each wave owns 32 query rows and computes S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16, so that every lane holds the scores of ONE
 //     query (column) for 16 keys per 32-key block: the row max and row sum are
@@ -664,14 +664,12 @@ int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus) {
     const int v = std::atoi(env);
     if (v == 4 || v == 8) return v;
   }
-  // Eight waves (256 query rows, three K/V stages, one workgroup per CU)
-  // halve the K/V traffic per query row and keep two tiles in flight; that
-  // wins while the grid is about one round of CUs (one frame of one stream).
-  // Once the 128-row tiles alone cover the CUs several times over (batched
-  // streams, multi-frame chunks), two 4-wave workgroups per CU hide each
-  // other's barriers and win instead.
-  const int64_t tiles4 = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + 127) / 128);
-  return tiles4 >= 4LL * num_cus ? 4 : 8;
+  // Eight waves (256 query rows, three K/V stages, one workgroup per CU):
+  // half the K/V traffic per query row of the four-wave shape, and measured
+  // faster for one stream and for batched multi-frame chunks alike.  Four
+  // waves (two workgroups per CU) stay available through SA_ATTN_WAVES.
+  (void)B; (void)H; (void)T; (void)n_q; (void)num_cus;
+  return 8;
 }
 
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus) {
