@@ -22,7 +22,8 @@
  *   synchronises the host except sa_rope_create (one table upload).
  * - Element types: SA_BF16 (bfloat16, round-to-nearest-even on every store)
  *   or SA_F32.  All arithmetic is fp32 (bf16 MFMA inputs, fp32 accumulation);
- *   RoPE angles are formed and range-reduced in fp64.
+ *   RoPE time-axis angles are formed and range-reduced in fp64 on the device,
+ *   grid-axis sines and cosines are evaluated in fp64 once, on the host.
  * - Every function returns an sa_status.  Arguments and state are validated
  *   before anything is changed or launched: on error the handle is left as it
  *   was and sa_last_error() (thread-local) describes the problem.
@@ -99,9 +100,11 @@ typedef struct sa_rope sa_rope;
  * output may be NULL. */
 sa_status sa_rope_tables(const sa_rope_desc* desc, double* theta_hat_out, double* freq_out);
 
-/* Validates desc, builds the fp64 frequency table and uploads it to the
- * current device (the only allocating / synchronising call of the library
- * besides this handle's destroy). */
+/* Validates desc, builds the fp64 frequency table and the cos/sin table of
+ * the grid-axis angles (row and column positions do not change from frame to
+ * frame; evaluated in fp64, stored in fp32) and uploads them to the current
+ * device (the only allocating / synchronising call of the library besides
+ * this handle's destroy). */
 sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out);
 void sa_rope_destroy(sa_rope* rope);
 

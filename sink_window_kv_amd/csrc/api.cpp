@@ -23,7 +23,9 @@ struct sa_rope {
   int dims[3];
   int grid_h, grid_w;
   sa::RopeTables tables;
-  double* d_freq = nullptr;  // device [H][D/2]
+  sa::RopeGridTable grid_table;
+  double* d_freq = nullptr;   // device [H][D/2]
+  float* d_grid = nullptr;    // device grid-axis cos/sin table (may stay null)
   int device = 0;
 };
 
@@ -90,9 +92,14 @@ sa_status check_rope_desc(const sa_rope_desc* d) {
 sa::RopeArgs rope_args(const sa_rope* r) {
   sa::RopeArgs a;
   a.freq = r->d_freq;
+  a.grid_cs = r->d_grid;
   a.pairs_t = r->dims[0] / 2;
   a.pairs_th = (r->dims[0] + r->dims[1]) / 2;
+  a.pairs_all = r->head_dim / 2;
+  a.grid_h = r->grid_h;
   a.grid_w = r->grid_w;
+  a.grid_stride = r->grid_table.stride;
+  a.grid_per_head = r->grid_table.per_head ? 1 : 0;
   return a;
 }
 
@@ -174,13 +181,22 @@ sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out) {
   r->grid_w = desc->grid_w;
   r->tables = sa::build_rope_tables(desc->n_heads, desc->head_dim, r->dims, desc->theta0,
                                     desc->sigma, desc->eps, desc->jitter_axes);
+  r->grid_table = sa::build_rope_grid_table(r->tables, desc->n_heads, desc->head_dim, r->dims, desc->grid_h,
+                                            desc->grid_w, desc->jitter_axes);
   hipError_t e = hipGetDevice(&r->device);
   if (e == hipSuccess) e = hipMalloc(&r->d_freq, r->tables.freq.size() * sizeof(double));
   if (e == hipSuccess)
     e = hipMemcpy(r->d_freq, r->tables.freq.data(), r->tables.freq.size() * sizeof(double),
                   hipMemcpyHostToDevice);
+  if (e == hipSuccess && !r->grid_table.cs.empty()) {
+    e = hipMalloc(&r->d_grid, r->grid_table.cs.size() * sizeof(float));
+    if (e == hipSuccess)
+      e = hipMemcpy(r->d_grid, r->grid_table.cs.data(), r->grid_table.cs.size() * sizeof(float),
+                    hipMemcpyHostToDevice);
+  }
   if (e != hipSuccess) {
     if (r->d_freq) (void)hipFree(r->d_freq);
+    if (r->d_grid) (void)hipFree(r->d_grid);
     delete r;
     return hip_fail(e, "sa_rope_create");
   }
@@ -191,6 +207,7 @@ sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out) {
 void sa_rope_destroy(sa_rope* r) {
   if (!r) return;
   if (r->d_freq) (void)hipFree(r->d_freq);
+  if (r->d_grid) (void)hipFree(r->d_grid);
   delete r;
 }
 
@@ -290,6 +307,15 @@ sa_status sa_cache_recache(sa_cache* c, const void* x, const void* w_k, const vo
   if ((2 * c->desc.n_heads * c->desc.head_dim) % 128 != 0)
     return fail(SA_ERR_SHAPE, "2 * n_heads * head_dim must be a multiple of 128");
   if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "recache on an empty cache");
+  {
+    // the bf16 kernel addresses x and each weight matrix with 32-bit byte offsets
+    const unsigned long long n_tok = static_cast<unsigned long long>(c->desc.batch) *
+                                     c->plan.resident().size() * c->desc.tokens_per_frame;
+    const unsigned long long hd = static_cast<unsigned long long>(c->desc.n_heads) * c->desc.head_dim;
+    const unsigned long long es = c->desc.dtype == SA_BF16 ? 2ull : 4ull;
+    if (n_tok * hidden * es >= (1ull << 32) || hd * hidden * es >= (1ull << 32))
+      return fail(SA_ERR_SHAPE, "x or a weight matrix reaches 4 GiB");
+  }
   sa::RecacheArgs a;
   a.x = x;
   a.wk = w_k;

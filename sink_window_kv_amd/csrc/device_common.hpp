@@ -63,15 +63,32 @@ __device__ __forceinline__ void rope_sincos(double pos, double w, float* s, floa
   sincosf(static_cast<float>(r), s, c);
 }
 
-// Rotate 4 adjacent pairs (8 channels starting at channel 8*chunk) in place:
-// (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
-__device__ __forceinline__ void rope_rotate8(const RopeArgs& r, const double* freq_h, int chunk,
-                                             int64_t t, int row, int col, float x[8]) {
+// sin and cos of channel pair p's angle for head h at (t, row, col): the
+// time axis is evaluated here (the angle depends on the frame); the grid
+// axes come from the precomputed table when there is one.
+__device__ __forceinline__ void rope_cs(const RopeArgs& r, int h, int p, int64_t t, int row, int col,
+                                        float* s, float* c) {
+  if (p < r.pairs_t || r.grid_cs == nullptr) {
+    rope_sincos(rope_pair_pos(r, p, t, row, col), r.freq[static_cast<size_t>(h) * r.pairs_all + p], s, c);
+    return;
+  }
+  const int ph = r.pairs_th - r.pairs_t;
+  const int idx = p < r.pairs_th ? row * ph + (p - r.pairs_t)
+                                 : r.grid_h * ph + col * (r.pairs_all - r.pairs_th) + (p - r.pairs_th);
+  const float2 v = reinterpret_cast<const float2*>(r.grid_cs)[(r.grid_per_head ? h * r.grid_stride : 0) + idx];
+  *c = v.x;
+  *s = v.y;
+}
+
+// Rotate 4 adjacent pairs (8 channels starting at channel 8*chunk) of head h
+// in place: (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
+__device__ __forceinline__ void rope_rotate8(const RopeArgs& r, int h, int chunk, int64_t t, int row, int col,
+                                             float x[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = chunk * 4 + i;
     float s, c;
-    rope_sincos(rope_pair_pos(r, p, t, row, col), freq_h[p], &s, &c);
+    rope_cs(r, h, p, t, row, col, &s, &c);
     const float x0 = x[2 * i], x1 = x[2 * i + 1];
     x[2 * i] = x0 * c - x1 * s;
     x[2 * i + 1] = x0 * s + x1 * c;

@@ -14,10 +14,14 @@ enum ElemType : int { kBF16 = 0, kF32 = 1 };
 
 // Device view of a RoPE handle.
 struct RopeArgs {
-  const double* freq;  // device [H][D/2], fp64
-  int32_t pairs_t;     // pairs [0, pairs_t) rotate with the time position
-  int32_t pairs_th;    // pairs [pairs_t, pairs_th) with the grid row, the rest with the column
-  int32_t grid_w;
+  const double* freq;   // device [H][D/2], fp64
+  const float* grid_cs; // device cos/sin of the grid-axis angles (see build_rope_grid_table), or null
+  int32_t pairs_t;      // pairs [0, pairs_t) rotate with the time position
+  int32_t pairs_th;     // pairs [pairs_t, pairs_th) with the grid row, the rest with the column
+  int32_t pairs_all;    // D / 2
+  int32_t grid_h, grid_w;
+  int32_t grid_stride;  // entries per head table
+  int32_t grid_per_head;
 };
 
 // Per-call table of frames, passed by value as a kernel argument.

@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) rope3d_kernel(RopeArgs rope, const E* __r
     const int tok = static_cast<int>(i - static_cast<int64_t>(j) * T);
     float v[8];
     load8(x + idx * 8, v);
-    rope_rotate8(rope, rope.freq + static_cast<size_t>(h) * (D / 2), c, t0 + j, tok / rope.grid_w,
+    rope_rotate8(rope, h, c, t0 + j, tok / rope.grid_w,
                  tok % rope.grid_w, v);
     store8(y + idx * 8, v);
   }
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) append_k_kernel(RopeArgs rope, CacheGeom 
     const int tok = static_cast<int>(i - static_cast<int64_t>(j) * g.T);
     float v[8];
     load8(k + idx * 8, v);
-    rope_rotate8(rope, rope.freq + static_cast<size_t>(h) * (g.D / 2), c, chunk.t[j],
+    rope_rotate8(rope, h, c, chunk.t[j],
                  tok / rope.grid_w, tok % rope.grid_w, v);
     const int64_t dst =
         ((((static_cast<int64_t>(chunk.store_slot[j]) * g.B + b) * g.H + h) * g.T + tok) * g.D) +
@@ -183,7 +183,6 @@ __global__ void __launch_bounds__(256) append_kv_bf16_kernel(RopeArgs rope, Cach
   const uint32_t blk = ((static_cast<uint32_t>(slot) * g.B + b) * g.H + h) * static_cast<uint32_t>(T) * D;
   uint16_t* kst = static_cast<uint16_t*>(g.k_store);
   uint16_t* vst = static_cast<uint16_t*>(g.v_store);
-  const double* freq_h = rope.freq + static_cast<size_t>(h) * (D / 2);
   const int64_t t = chunk.t[j];
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
@@ -194,7 +193,7 @@ __global__ void __launch_bounds__(256) append_kv_bf16_kernel(RopeArgs rope, Cach
     if (tok < T) {
       float x[8];
       unpack_bf16x8(kv[u], x);
-      rope_rotate8(rope, freq_h, d0 / 8 + cv, t, tok / rope.grid_w, tok % rope.grid_w, x);
+      rope_rotate8(rope, h, d0 / 8 + cv, t, tok / rope.grid_w, tok % rope.grid_w, x);
       *reinterpret_cast<u32x4*>(kst + blk + static_cast<uint32_t>(tok) * D + d0 + cv * VE) = pack_bf16x8(x);
     }
   }

@@ -45,4 +45,48 @@ inline RopeTables build_rope_tables(int n_heads, int head_dim, const int dims[3]
   return t;
 }
 
+// cos and sin of the grid-axis angles, which do not depend on the frame:
+// for every head table (one per head when the h or w axis is jittered, else
+// one shared), entries [row][pairs_h] then [col][pairs_w], each (cos, sin) of
+// pos * w formed and evaluated in fp64, rounded to fp32.  Empty when the
+// table would exceed max_bytes (the kernels then evaluate sin/cos directly).
+struct RopeGridTable {
+  std::vector<float> cs;  // [n_tab][stride][2]
+  int stride = 0;         // entries per head table
+  bool per_head = false;
+};
+
+inline RopeGridTable build_rope_grid_table(const RopeTables& t, int n_heads, int head_dim, const int dims[3],
+                                           int grid_h, int grid_w, uint32_t jitter_axes,
+                                           size_t max_bytes = size_t(32) << 20) {
+  if (jitter_axes == 0) jitter_axes = 1u;
+  RopeGridTable g;
+  const int pt = dims[0] / 2, ph = dims[1] / 2, pw = dims[2] / 2;
+  g.per_head = (jitter_axes & 6u) != 0;
+  g.stride = grid_h * ph + grid_w * pw;
+  const int n_tab = g.per_head ? n_heads : 1;
+  if (static_cast<size_t>(n_tab) * g.stride * 2 * sizeof(float) > max_bytes) {
+    g.stride = 0;
+    return g;
+  }
+  g.cs.resize(static_cast<size_t>(n_tab) * g.stride * 2);
+  const size_t hp = static_cast<size_t>(head_dim / 2);
+  for (int h = 0; h < n_tab; ++h) {
+    float* out = g.cs.data() + static_cast<size_t>(h) * g.stride * 2;
+    for (int row = 0; row < grid_h; ++row)
+      for (int j = 0; j < ph; ++j, out += 2) {
+        const double a = static_cast<double>(row) * t.freq[h * hp + pt + j];
+        out[0] = static_cast<float>(std::cos(a));
+        out[1] = static_cast<float>(std::sin(a));
+      }
+    for (int col = 0; col < grid_w; ++col)
+      for (int j = 0; j < pw; ++j, out += 2) {
+        const double a = static_cast<double>(col) * t.freq[h * hp + pt + ph + j];
+        out[0] = static_cast<float>(std::cos(a));
+        out[1] = static_cast<float>(std::sin(a));
+      }
+  }
+  return g;
+}
+
 }  // namespace sa

@@ -230,7 +230,6 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   // ---- Q fragment: rotate in fp32, round to bf16 (B operand of S^T = K Q^T).
   mfma_bf16x8 qfrag[D / 16];
   {
-    const double* freq_h = a.rope.freq + static_cast<size_t>(h) * (D / 2);
     const int tok = row_ok ? row - qf * T : 0;
     const int64_t t = a.frames.t[first_q + qf];
     const uint16_t* qrow =
@@ -241,7 +240,7 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
       if (row_ok) {
         float x[8];
         unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
-        rope_rotate8(a.rope, freq_h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+        rope_rotate8(a.rope, h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
         v = pack_bf16x8(x);
       }
       qfrag[s] = as_bf16x8(v);
@@ -587,13 +586,12 @@ __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
     const int tok = row_ok ? row - qf * T : 0;
     const int64_t t = a.frames.t[first_q + qf];
     const float* qrow = static_cast<const float*>(a.q) + ((static_cast<int64_t>(b) * Lq + (row_ok ? row : 0)) * g.H + h) * D;
-    const double* freq_h = a.rope.freq + static_cast<size_t>(h) * (D / 2);
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = row_ok ? qrow[c * 8 + i] : 0.f;
-      rope_rotate8(a.rope, freq_h, c, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+      rope_rotate8(a.rope, h, c, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[c * 8 + i] = x[i];
     }
