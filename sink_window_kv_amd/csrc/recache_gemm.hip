@@ -22,10 +22,10 @@ namespace {
 typedef __bf16 mfma_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float mfma_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
-constexpr int kTM = 512;    // features per workgroup
+constexpr int kTM = 256;    // features per workgroup
 constexpr int kTN = 128;    // tokens per workgroup
 constexpr int kTK = 32;     // reduction slice per LDS stage
-constexpr int kGWaves = 8;  // waves per workgroup (4 x 2 grid of 128 x 64 wave tiles)
+constexpr int kGWaves = 4;  // waves per workgroup (2 x 2 grid of 128 x 64 wave tiles)
 constexpr int kAI = kTM * 4 / (kGWaves * 64);  // feature-tile transfers per wave per slice
 constexpr int kBI = kTN * 4 / (kGWaves * 64);  // token-tile transfers per wave per slice
 static_assert(kAI * kGWaves * 64 == kTM * 4 && kBI * kGWaves * 64 == kTN * 4, "whole tiles");
@@ -86,13 +86,12 @@ __device__ __forceinline__ void token_coords(int64_t n, int per_stream, int T, i
   *tok = rem - *lf * T;
 }
 
-// Workgroup: 512 features x 128 tokens, eight waves in a 4 x 2 grid, each
-// 128 features x 64 tokens (4 x 2 products of 32 x 32).  The tall feature
-// tile halves how often each token row of x is streamed in (once per 512
-// output features).  The reduction runs
+// Workgroup: 256 features x 128 tokens, four waves in a 2 x 2 grid, each
+// 128 features x 64 tokens (4 x 2 products of 32 x 32); two workgroups per
+// CU, so one's epilogue overlaps the other's products.  The reduction runs
 // in slices of 32 through two LDS stages filled by direct-to-LDS loads: the
 // next slice lands while the current one is multiplied.
-__global__ void __launch_bounds__(kGWaves * 64, 1) recache_bf16_kernel(RecacheArgs a) {
+__global__ void __launch_bounds__(kGWaves * 64, 2) recache_bf16_kernel(RecacheArgs a) {
   __shared__ GemmSmem sm;
   GemmStage* stg = sm.stg;
   const CacheGeom& g = a.g;
