@@ -146,3 +146,39 @@ def test_recache_errors():
     with pytest.raises(swk.SinkAttnError) as e:
         swk.sa_cache_recache(gs.cache, x, wk, wk, 60)
     assert e.value.status == swk.SA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("n_heads,head_dim,dims,grid,hidden", [
+    # 2*H*D = 384: the K/V boundary (192) falls inside the first 256-feature
+    # tile and the second tile is half padding; 576 tokens = 4.5 token tiles;
+    # hidden 192 = 6 reduction slices
+    (3, 64, (22, 22, 20), (6, 12), 192),
+    # 2*H*D = 640 (2.5 feature tiles, boundary at 320 inside the second);
+    # tokens per frame 40 so 128-token tiles cross frames and streams
+    (5, 64, (22, 22, 20), (4, 10), 320),
+])
+def test_recache_bf16_ragged_tiles(n_heads, head_dim, dims, grid, hidden):
+    """bf16 recache where features and tokens do not fill whole GEMM tiles, with a wrapped ring."""
+    import torch
+    swk = _swk()
+    w = wl.Workload("recache-ragged", 45, batch=2, n_heads=n_heads, head_dim=head_dim, dims=dims, grid=grid,
+                    n_sink=1, n_local=3, chunk=1, frames=7, dtype="bf16", sigma=0.8, hidden=hidden)
+    eps = wl.head_jitter(w)
+    gs = GpuStream(w, eps=eps)
+    for f in range(w.frames):
+        gs.append(wl.frame_qkv(w, f, tensor=wl.TENSOR_K), wl.frame_qkv(w, f, tensor=wl.TENSOR_V), 1, f)
+    res = gs.oracle.resident()
+    x, wk, wv = wl.recache_inputs(w, n_frames=len(res))
+    log(f"recache ragged H={n_heads} D={head_dim} grid={grid} hidden={hidden} resident={res}")
+    swk.sa_cache_recache(gs.cache, to_dev(x, "bf16"), to_dev(np.ascontiguousarray(wk.T), "bf16"),
+                         to_dev(np.ascontiguousarray(wv.T), "bf16"), w.hidden)
+    torch.cuda.synchronize()
+    gs.oracle.recache(x, wk, wv)
+    for i, f in enumerate(res):
+        ko, vo = _read_frame(gs, i)
+        kref, vref = gs.oracle.frame_kv(f)
+        assert_close(to_np(ko), kref, "bf16", f"ragged recache K frame {f}")
+        assert_close(to_np(vo), vref, "bf16", f"ragged recache V frame {f}")
+    q = wl.frame_qkv(w, w.frames - 1, tensor=wl.TENSOR_Q)
+    o = gs.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
+    _check(gs, q, o, True, what="attention after ragged recache")
