@@ -20,6 +20,10 @@ float64, written from the pages:
                    attention" equation).
 * ``recache``   -- K, V = x W_k, x W_v over the cached frames, K re-rotated
                    (LongLive paper review, section 3 "KV Recache").
+* ``project``   -- per-frame q, k, v = x W_q, x W_k, x W_v with (k, v)
+                   appended to the cache, and a plain linear map x W
+                   (LoL paper review, background "multi-head attention";
+                   LongLive paper review, section 3 "KV Recache").
 * ``brute``     -- pure-Python loop versions for tiny shapes, used to pin the
                    numpy versions.
 * ``stream``    -- composes the above into the per-frame stream the library
@@ -28,4 +32,4 @@ float64, written from the pages:
 Pins (tests/test_oracle_*.py) tie these to closed forms, invariants,
 library routines and brute force; see the test docstrings.
 """
-from . import rope, cache, attention, recache, brute, stream  # noqa: F401
+from . import rope, cache, attention, recache, project, brute, stream  # noqa: F401

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from oracle import attention as oattn
-from oracle import brute, cache as ocache, recache as orecache, rope as orope, stream as ostream
+from oracle import brute, cache as ocache, project as oproject, recache as orecache, rope as orope, stream as ostream
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(1234)
@@ -262,6 +262,79 @@ def test_p6_recache_with_unchanged_weights_reproduces_cache():
         np.testing.assert_allclose(so.frame_kv(f)[1][0].reshape(T, H * D),
                                    torch.from_numpy(x_all[0, j * T:(j + 1) * T]) .matmul(torch.from_numpy(w_new)).numpy(),
                                    atol=1e-12)
+
+
+# ------------------------------------------------------------ P9 projections
+def _perm_matrix(perm):
+    """Column-selection matrix: (x . P)[..., j] = x[..., perm[j]]."""
+    n = len(perm)
+    p = np.zeros((n, n))
+    for j, i in enumerate(perm):
+        p[i, j] = 1.0
+    return p
+
+
+def test_p9_linear_matches_brute_force_and_selection():
+    """x . W (LoL paper review, background "multi-head attention" projections): brute-force loops on a
+    non-square W, and a selection matrix picks columns (a transposed W would pick the inverse permutation)."""
+    x = RNG.standard_normal((2, 5, 6))
+    w = RNG.standard_normal((6, 4))
+    y = oproject.linear(x, w)
+    assert y.shape == (2, 5, 4)
+    for b in range(2):
+        np.testing.assert_allclose(y[b], brute.matvec_rows(x[b].tolist(), w.tolist()), rtol=0, atol=1e-12)
+    perm = [2, 0, 5, 1, 3, 4]     # not its own inverse
+    np.testing.assert_array_equal(oproject.linear(x, _perm_matrix(perm)), x[..., perm])
+    np.testing.assert_array_equal(oproject.linear(x, np.eye(6)), x)
+
+
+def test_p9_project_append_with_selection_weights_is_plain_append():
+    """With permutation weights the projections reduce to appending the permuted inputs: same cache,
+    same slots, same evictions, q = the permuted x (the append path is pinned by P3, P4 and P8)."""
+    bases, dims, grid = _tiny_setup(H=2, dims=(4, 2, 2), grid=(2, 2))
+    T, H, D = 4, 2, 8
+    C = H * D
+    pq, pk, pv = (list(RNG.permutation(C)) for _ in range(3))
+    a = ostream.StreamOracle(1, 3, T, grid[1], dims, bases)
+    b = ostream.StreamOracle(1, 3, T, grid[1], dims, bases)
+    t0 = 3
+    for c in (1, 2, 1, 3, 2):
+        x = RNG.standard_normal((2, c * T, C))
+        q, ev_a = oproject.project_append(a, x, _perm_matrix(pq), _perm_matrix(pk), _perm_matrix(pv), H, t0)
+        ev_b = b.append(x[..., pk].reshape(2, c * T, H, D), x[..., pv].reshape(2, c * T, H, D), t0)
+        assert ev_a == ev_b
+        np.testing.assert_array_equal(q, x[..., pq].reshape(2, c * T, H, D))
+        assert a.resident() == b.resident()
+        for f in a.resident():
+            np.testing.assert_array_equal(a.frame_kv(f)[0], b.frame_kv(f)[0])
+            np.testing.assert_array_equal(a.frame_kv(f)[1], b.frame_kv(f)[1])
+        t0 += c + 2
+    q, _ = oproject.project_append(a, RNG.standard_normal((2, T, C)), None, np.eye(C), np.eye(C), H, t0)
+    assert q is None
+
+
+def test_p9_project_append_brute_force():
+    """Brute-force loops: q = x W_q, K = RoPE(x W_k, t_f) per head and token, V = x W_v."""
+    bases, dims, grid = _tiny_setup(H=2, dims=(4, 2, 2), grid=(2, 2))
+    T, H, D, C = 4, 2, 8, 5
+    w_q, w_k, w_v = (RNG.standard_normal((C, H * D)) for _ in range(3))
+    so = ostream.StreamOracle(1, 2, T, grid[1], dims, bases)
+    x = RNG.standard_normal((1, 2 * T, C))
+    t0 = 7
+    q, _ = oproject.project_append(so, x, w_q, w_k, w_v, H, t0)
+    qb = brute.matvec_rows(x[0].tolist(), w_q.tolist())
+    kb = brute.matvec_rows(x[0].tolist(), w_k.tolist())
+    vb = brute.matvec_rows(x[0].tolist(), w_v.tolist())
+    np.testing.assert_allclose(q[0].reshape(2 * T, H * D), qb, rtol=0, atol=1e-12)
+    for j, f in enumerate(so.resident()):
+        kf, vf = so.frame_kv(f)
+        for tok in range(T):
+            row = j * T + tok
+            np.testing.assert_allclose(vf[0, tok].reshape(H * D), vb[row], rtol=0, atol=1e-12)
+            for h in range(H):
+                ref = brute.rope_vector(kb[row][h * D:(h + 1) * D], brute.positions(t0 + j, tok, grid[1], dims),
+                                        brute.frequencies(bases[h], dims))
+                np.testing.assert_allclose(kf[0, tok, h], ref, rtol=0, atol=1e-12)
 
 
 # ------------------------------------------------------------ P7 closed forms
