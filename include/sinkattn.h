@@ -176,10 +176,40 @@ sa_status sa_cache_append(sa_cache* cache, const void* k, const void* v, int32_t
  *                                     logical order (sinks, then local oldest -> newest)
  *   w_k, w_v [H*D, hidden]            projection weights in the nn.Linear
  *                                     [out, in] layout: row h*D+d makes channel d of head h
- * All of the cache's dtype.  hidden must be a multiple of 64.  SA_ERR_STATE on
+ * All of the cache's dtype.  hidden must be a multiple of 32.  SA_ERR_STATE on
  * an empty cache. */
 sa_status sa_cache_recache(sa_cache* cache, const void* x, const void* w_k, const void* w_v,
                            int32_t hidden, void* stream);
+
+/* Per-frame projections of a new chunk, fused with its append ([LoL]
+ * background "multi-head attention": each head's own query, key and value
+ * projections; [LongLive] section 3 "KV Recache" re-runs the same key/value
+ * maps over the cached frames):
+ *   q = x . W_q^T (written to q_out, un-rotated: sa_window_attn rotates its
+ *   queries), and the frames' k = x . W_k^T, v = x . W_v^T are appended with
+ *   times t0 .. t0+n_frames-1 exactly as sa_cache_append would append them
+ *   (K rotated, sinks pinned, ring eviction), without k and v ever being
+ *   written to memory in between.
+ *   x      [B, n_frames*T_f, hidden]  hidden states of the new frames
+ *   w_q, w_k, w_v [H*D, hidden]       [out, in] layout; row h*D+d makes
+ *                                     channel d of head h
+ *   q_out  [B, n_frames*T_f, H, D]    may be NULL together with w_q (then
+ *                                     only the cache is written)
+ * All of the cache's dtype.  hidden must be a multiple of 32.  The same
+ * chunk and time rules as sa_cache_append apply (SA_ERR_RANGE/SHAPE). */
+sa_status sa_cache_project_append(sa_cache* cache, const void* x, const void* w_q, const void* w_k,
+                                  const void* w_v, int32_t hidden, void* q_out, int32_t n_frames,
+                                  int64_t t0, void* stream);
+
+/* Plain linear map y = x . W^T, e.g. the output projection that follows the
+ * attention in a multi-head attention block (the reviewed pages show none;
+ * no bias):
+ *   x [n_rows, in_features], w [out_features, in_features] ([out, in]
+ *   layout), y [n_rows, out_features]; all of element type dtype.
+ * in_features must be a multiple of 32, out_features a multiple of 16;
+ * n_rows may be 0 (nothing is launched).  y must not overlap x or w. */
+sa_status sa_linear(const void* x, const void* w, void* y, sa_dtype dtype, int64_t n_rows,
+                    int32_t in_features, int32_t out_features, void* stream);
 
 /* Workspace sa_window_attn needs for this cache state and n_q (may be 0). */
 sa_status sa_window_attn_workspace(const sa_cache* cache, int32_t n_q, size_t* bytes);

@@ -66,6 +66,9 @@ _SIGNATURES = {
     "sa_cache_reset": (ctypes.c_int, [_VP]),
     "sa_cache_append": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.c_int64, _VP]),
     "sa_cache_recache": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int32, _VP]),
+    "sa_cache_project_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, ctypes.c_int32,
+                                               ctypes.c_int64, _VP]),
+    "sa_linear": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _VP]),
     "sa_window_attn_workspace": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "sa_window_attn": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _VP,
                                       ctypes.c_size_t, _VP]),
@@ -235,6 +238,22 @@ def sa_cache_recache(cache: Cache, x, w_k, w_v, hidden: int, stream=None):
     """w_k, w_v in the [H*D, hidden] (nn.Linear) layout."""
     _check(lib().sa_cache_recache(cache.handle, _ptr(x), _ptr(w_k), _ptr(w_v), hidden, _stream(stream)),
            "sa_cache_recache")
+
+
+def sa_cache_project_append(cache: Cache, x, w_q, w_k, w_v, hidden: int, q_out, n_frames: int, t0: int,
+                            stream=None):
+    """q_out = x . w_q^T (un-rotated); k = x . w_k^T, v = x . w_v^T appended at t0...; weights [H*D, hidden].
+
+    w_q and q_out may both be None (cache only).
+    """
+    _check(lib().sa_cache_project_append(cache.handle, _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), hidden,
+                                         _ptr(q_out), n_frames, t0, _stream(stream)), "sa_cache_project_append")
+
+
+def sa_linear(x, w, y, n_rows: int, in_features: int, out_features: int, stream=None):
+    """y [n_rows, out] = x [n_rows, in] . w^T, w in the [out, in] layout."""
+    _check(lib().sa_linear(_ptr(x), _ptr(w), _ptr(y), _dtype_code(x), n_rows, in_features, out_features,
+                           _stream(stream)), "sa_linear")
 
 
 def sa_window_attn_workspace(cache: Cache, n_q: int) -> int:

@@ -126,6 +126,63 @@ sa::FrameTable resident_table(const sa_cache* c) {
   return ft;
 }
 
+// Chunk rules shared by the two append paths (t0 range checked by the caller).
+sa_status check_append_chunk(const sa_cache* c, int32_t n_frames, int64_t t0) {
+  switch (c->plan.check_append(n_frames, t0)) {
+    case 0: return SA_OK;
+    case 1: return fail(SA_ERR_SHAPE, "n_frames must be in [1, %d]", SA_MAX_FRAMES);
+    case 2: return fail(SA_ERR_RANGE, "chunk of %d frames does not fit the %d-frame local window", n_frames,
+                        c->desc.n_local);
+    default: return fail(SA_ERR_RANGE, "t0 (%lld) must exceed the newest cached time (%lld)",
+                         static_cast<long long>(t0), static_cast<long long>(c->plan.newest_t()));
+  }
+}
+
+// Slots and times the next append of n_frames frames at t0 will use.
+sa::FrameTable chunk_table(const sa_cache* c, int32_t n_frames, int64_t t0) {
+  const auto planned = c->plan.plan_append(n_frames, t0);
+  sa::FrameTable chunk{};
+  chunk.n = n_frames;
+  for (int i = 0; i < n_frames; ++i) {
+    chunk.store_slot[i] = planned[i].store_slot;
+    chunk.t[i] = planned[i].t;
+  }
+  return chunk;
+}
+
+// Size rules of the projection GEMM: the reduction runs in slices of 32,
+// and the bf16 kernel addresses x and each weight matrix with 32-bit byte
+// offsets (rows past the end included).
+sa_status check_proj_sizes(int64_t n_tok, int32_t hidden, int32_t width, size_t es) {
+  if (hidden < 32 || hidden % 32 != 0 || hidden > (1 << 16))
+    return fail(SA_ERR_SHAPE, "hidden / in_features must be a multiple of 32 in [32, 65536]");
+  const unsigned long long row = static_cast<unsigned long long>(hidden) * es;
+  if ((static_cast<unsigned long long>(n_tok) + 256) * row >= (1ull << 32) ||
+      (static_cast<unsigned long long>(width) + 256) * row >= (1ull << 32))
+    return fail(SA_ERR_SHAPE, "x or a weight matrix reaches 4 GiB");
+  return SA_OK;
+}
+
+// Projection segments into this cache: [q rows,] rotated keys, values.
+sa::ProjArgs cache_proj_args(const sa_cache* c, const void* x, const void* w_q, void* q_out, const void* w_k,
+                             const void* w_v, int32_t hidden) {
+  sa::ProjArgs a{};
+  a.x = x;
+  a.hidden = hidden;
+  a.width = c->desc.n_heads * c->desc.head_dim;
+  int n = 0;
+  if (w_q) a.seg[n++] = sa::ProjSeg{w_q, q_out, sa::kOutRows};
+  a.seg[n++] = sa::ProjSeg{w_k, nullptr, sa::kOutCacheK};
+  a.seg[n++] = sa::ProjSeg{w_v, nullptr, sa::kOutCacheV};
+  a.n_seg = n;
+  for (int i = n; i < 3; ++i) a.seg[i] = a.seg[n - 1];
+  a.has_key = 1;
+  a.has_value = 1;
+  a.g = geom(c);
+  a.rope = rope_args(c->rope);
+  return a;
+}
+
 int device_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -276,21 +333,8 @@ sa_status sa_cache_append(sa_cache* c, const void* k, const void* v, int32_t n_f
   if (!c || !k || !v) return fail(SA_ERR_NULL, "cache, k and v must be non-NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(SA_ERR_ALIGN, "k and v must be 16-byte aligned");
   if (t0 < 0 || t0 > (int64_t(1) << 40)) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40]");
-  switch (c->plan.check_append(n_frames, t0)) {
-    case 0: break;
-    case 1: return fail(SA_ERR_SHAPE, "n_frames must be in [1, %d]", SA_MAX_FRAMES);
-    case 2: return fail(SA_ERR_RANGE, "chunk of %d frames does not fit the %d-frame local window", n_frames,
-                        c->desc.n_local);
-    default: return fail(SA_ERR_RANGE, "t0 (%lld) must exceed the newest cached time (%lld)",
-                         static_cast<long long>(t0), static_cast<long long>(c->plan.newest_t()));
-  }
-  const auto planned = c->plan.plan_append(n_frames, t0);
-  sa::FrameTable chunk{};
-  chunk.n = n_frames;
-  for (int i = 0; i < n_frames; ++i) {
-    chunk.store_slot[i] = planned[i].store_slot;
-    chunk.t[i] = planned[i].t;
-  }
+  if (sa_status s = check_append_chunk(c, n_frames, t0)) return s;
+  const sa::FrameTable chunk = chunk_table(c, n_frames, t0);
   const hipError_t e = sa::launch_append(rope_args(c->rope), geom(c), k, v, c->desc.dtype, chunk,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
@@ -302,30 +346,66 @@ sa_status sa_cache_recache(sa_cache* c, const void* x, const void* w_k, const vo
                            void* stream) {
   if (!c || !x || !w_k || !w_v) return fail(SA_ERR_NULL, "cache, x, w_k and w_v must be non-NULL");
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v)) return fail(SA_ERR_ALIGN, "x and weights must be 16-byte aligned");
-  if (hidden < 64 || hidden % 64 != 0 || hidden > (1 << 16))
-    return fail(SA_ERR_SHAPE, "hidden must be a multiple of 64 in [64, 65536]");
-  if ((2 * c->desc.n_heads * c->desc.head_dim) % 128 != 0)
-    return fail(SA_ERR_SHAPE, "2 * n_heads * head_dim must be a multiple of 128");
+  const int hd = c->desc.n_heads * c->desc.head_dim;
+  if (sa_status s = check_proj_sizes(0, hidden, hd, elem_size(c->desc.dtype))) return s;
   if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "recache on an empty cache");
-  {
-    // the bf16 kernel addresses x and each weight matrix with 32-bit byte offsets
-    const unsigned long long n_tok = static_cast<unsigned long long>(c->desc.batch) *
-                                     c->plan.resident().size() * c->desc.tokens_per_frame;
-    const unsigned long long hd = static_cast<unsigned long long>(c->desc.n_heads) * c->desc.head_dim;
-    const unsigned long long es = c->desc.dtype == SA_BF16 ? 2ull : 4ull;
-    if (n_tok * hidden * es >= (1ull << 32) || hd * hidden * es >= (1ull << 32))
-      return fail(SA_ERR_SHAPE, "x or a weight matrix reaches 4 GiB");
-  }
-  sa::RecacheArgs a;
-  a.x = x;
-  a.wk = w_k;
-  a.wv = w_v;
-  a.hidden = hidden;
-  a.g = geom(c);
-  a.rope = rope_args(c->rope);
+  const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * c->plan.resident().size() * c->desc.tokens_per_frame;
+  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, elem_size(c->desc.dtype))) return s;
+  sa::ProjArgs a = cache_proj_args(c, x, nullptr, nullptr, w_k, w_v, hidden);
+  a.n_tok = n_tok;
   a.frames = resident_table(c);
-  const hipError_t e = sa::launch_recache(a, c->desc.dtype, static_cast<hipStream_t>(stream));
+  const hipError_t e = sa::launch_proj(a, c->desc.dtype, device_cus(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "recache launch");
+  return ok();
+}
+
+sa_status sa_cache_project_append(sa_cache* c, const void* x, const void* w_q, const void* w_k, const void* w_v,
+                                  int32_t hidden, void* q_out, int32_t n_frames, int64_t t0, void* stream) {
+  if (!c || !x || !w_k || !w_v) return fail(SA_ERR_NULL, "cache, x, w_k and w_v must be non-NULL");
+  if (!w_q != !q_out) return fail(SA_ERR_NULL, "w_q and q_out must both be given or both be NULL");
+  if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(w_q) || !aligned16(q_out))
+    return fail(SA_ERR_ALIGN, "x, weights and q_out must be 16-byte aligned");
+  if (t0 < 0 || t0 > (int64_t(1) << 40)) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40]");
+  if (sa_status s = check_append_chunk(c, n_frames, t0)) return s;
+  const int hd = c->desc.n_heads * c->desc.head_dim;
+  const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * n_frames * c->desc.tokens_per_frame;
+  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, elem_size(c->desc.dtype))) return s;
+  sa::ProjArgs a = cache_proj_args(c, x, w_q, q_out, w_k, w_v, hidden);
+  a.n_tok = n_tok;
+  a.frames = chunk_table(c, n_frames, t0);
+  const hipError_t e = sa::launch_proj(a, c->desc.dtype, device_cus(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  c->plan.commit_append(n_frames, t0);
+  return ok();
+}
+
+sa_status sa_linear(const void* x, const void* w, void* y, sa_dtype dtype, int64_t n_rows, int32_t in_features,
+                    int32_t out_features, void* stream) {
+  if (!x || !w || !y) return fail(SA_ERR_NULL, "x, w and y must be non-NULL");
+  if (dtype != SA_BF16 && dtype != SA_F32) return fail(SA_ERR_DTYPE, "dtype must be SA_BF16 or SA_F32");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(SA_ERR_ALIGN, "x, w and y must be 16-byte aligned");
+  if (n_rows < 0) return fail(SA_ERR_SHAPE, "n_rows must be >= 0");
+  if (out_features < 16 || out_features % 16 != 0 || out_features > (1 << 20))
+    return fail(SA_ERR_SHAPE, "out_features must be a multiple of 16 in [16, 2^20]");
+  if (sa_status s = check_proj_sizes(n_rows, in_features, out_features, elem_size(dtype))) return s;
+  const size_t es = elem_size(dtype);
+  const auto overlaps = [](const void* p, size_t pb, const void* q, size_t qb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+    return a0 < b0 + qb && b0 < a0 + pb;
+  };
+  const size_t yb = static_cast<size_t>(n_rows) * out_features * es;
+  if (n_rows > 0 && (overlaps(y, yb, x, static_cast<size_t>(n_rows) * in_features * es) ||
+                     overlaps(y, yb, w, static_cast<size_t>(out_features) * in_features * es)))
+    return fail(SA_ERR_RANGE, "y overlaps x or w");
+  sa::ProjArgs a{};
+  a.x = x;
+  a.n_tok = n_rows;
+  a.hidden = in_features;
+  a.width = out_features;
+  a.n_seg = 1;
+  for (int i = 0; i < 3; ++i) a.seg[i] = sa::ProjSeg{w, y, sa::kOutRows};
+  const hipError_t e = sa::launch_proj(a, dtype, device_cus(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
   return ok();
 }
 

@@ -54,14 +54,31 @@ struct AttnArgs {
   int32_t n_waves;       // waves per workgroup (bf16 kernel)
 };
 
-struct RecacheArgs {
-  const void* x;   // [B, n_res*T, C]
-  const void* wk;  // [H*D, C]
-  const void* wv;  // [H*D, C]
-  int32_t hidden;  // C
+// Projection GEMM: out[n][f] = sum_c x[n][c] W[f][c] over up to three
+// output segments of `width` features each (one weight matrix per segment).
+enum ProjOut : int {
+  kOutRows = 0,    // row-major [n_tok][width] at y
+  kOutCacheK = 1,  // rotated at the token's frame time, into the key store
+  kOutCacheV = 2,  // into the transposed value store
+};
+struct ProjSeg {
+  const void* w;  // [width][C]
+  void* y;        // kOutRows only
+  int32_t kind;   // ProjOut
+};
+struct ProjArgs {
+  const void* x;      // [n_tok][C]
+  int64_t n_tok;
+  int32_t hidden;     // C
+  int32_t width;      // features per segment (multiple of 16)
+  int32_t n_seg;      // 1..3; unused entries repeat a valid weight pointer
+  ProjSeg seg[3];
+  int32_t has_key, has_value;  // some segment is kOutCacheK / kOutCacheV
+  // Cache outputs only: token n is token tok of frame j of stream b, with
+  // n = (b * frames.n + j) * T + tok.
   CacheGeom g;
   RopeArgs rope;
-  FrameTable frames;  // resident frames, logical order
+  FrameTable frames;
 };
 
 hipError_t launch_rope3d(const RopeArgs& rope, const void* x, void* y, int dtype, int B, int H,
@@ -79,6 +96,9 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
 size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits);
 hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream);
 
-hipError_t launch_recache(const RecacheArgs& a, int dtype, hipStream_t stream);
+// Tile shape the bf16 projection kernel takes for n_tok x F outputs:
+// 0 = 256 x 128, 1 = 128 x 128, 2 = 128 x 64 (features x tokens).
+int proj_tile_shape(int64_t n_tok, int F, int num_cus);
+hipError_t launch_proj(const ProjArgs& a, int dtype, int num_cus, hipStream_t stream);
 
 }  // namespace sa

@@ -1,0 +1,430 @@
+// Projection GEMMs around the attention: one matrix-core kernel with three
+// kinds of output segment.
+//
+//   out^T[f][n] = sum_c W[f][c] x[n][c]
+//
+// Weights are in the [out, in] layout, so both operands are contiguous along
+// the reduction axis, as the matrix cores want.  The output features are
+// the concatenation of up to three segments of equal width (one weight
+// matrix each); a segment's result either goes to a plain row-major matrix
+// [token][feature], or straight into the frame cache:
+//   * key segment: each key channel pair is rotated at its token's frame
+//     time (RoPE, same device code as the append kernel) and the result is
+//     scattered to the key store [slot][b][h][tok][d];
+//   * value segment: scattered to the transposed value store
+//     [slot][b][h][d][tok].
+// Three entry points use it:
+//   * KV recache at a prompt switch (LongLive paper review, section 3 "KV
+//     Recache"): segments (W_k -> key cache, W_v -> value cache) over every
+//     resident token;
+//   * per-frame projections of a new chunk (LoL paper review, background
+//     "multi-head attention": every head has its own query, key and value
+//     projections): (W_q -> q rows, W_k -> key cache, W_v -> value cache),
+//     the cache writes being the append of the new frames;
+//   * a plain linear map (one row-major segment), e.g. the output
+//     projection after the attention.
+// The feature-major orientation puts 4 consecutive channels of one token in
+// each lane, so every RoPE pair is in-lane.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+
+#include "device_common.hpp"
+
+namespace sa {
+namespace {
+
+typedef __bf16 mfma_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float mfma_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int kTK = 32;     // reduction slice per LDS stage
+constexpr int kGWaves = 4;  // waves per workgroup, a 2 x 2 grid of wave tiles
+constexpr int kOPad = 8;    // epilogue tile row padding (bf16 elements)
+#ifndef PROJ_PRE
+#define PROJ_PRE 3
+#endif
+constexpr int kPre = PROJ_PRE;  // reduction slices in flight in registers
+
+// LDS stage: rows of kTK bf16 = 4 chunks of 16 bytes, chunk (r, c) stored at
+// r*4 + (c ^ swz(r)).  A 16-byte LDS read is served 16 lanes at a time, and
+// the 16 lanes of an operand read take 16 consecutive rows at one chunk
+// index: 4 rows share each 256-byte line of the 64 banks, and the swizzle
+// gives those 4 rows 4 different chunk positions, so every 16-lane group
+// hits each bank once.
+template <int TM, int TN>
+struct GemmStage {
+  u32x4 a[TM * 4];  // features x reduction slice
+  u32x4 b[TN * 4];  // tokens x reduction slice
+};
+__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
+// Epilogue tile: the workgroup's results in bf16, [token][feature] (padded
+// rows), so that every output layout is written in whole 16-byte pieces.
+template <int TM, int TN>
+struct GemmOut {
+  uint16_t o[TN][TM + kOPad];
+};
+template <int TM, int TN>
+union GemmSmem {
+  GemmStage<TM, TN> stg[2];
+  GemmOut<TM, TN> out;
+};
+
+__device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(mfma_bf16x8, v);
+}
+
+// Map a global token index to (stream, frame of the table, token in frame).
+__device__ __forceinline__ void token_coords(int64_t n, int per_stream, int T, int* b, int* lf,
+                                             int* tok) {
+  *b = static_cast<int>(n / per_stream);
+  const int rem = static_cast<int>(n - static_cast<int64_t>(*b) * per_stream);
+  *lf = rem / T;
+  *tok = rem - *lf * T;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           static_cast<int>(static_cast<uint32_t>(bytes)), 0x00020000);
+}
+
+// Workgroup: TM features x TN tokens, four waves in a 2 x 2 grid, each
+// (TM/2) x (TN/2) as (TM/64) x (TN/64) products of 32 x 32; two workgroups
+// per CU, so one's epilogue overlaps the other's products.  The reduction
+// runs in slices of 32: each step writes the next slice (already in
+// registers) into the free LDS stage, loads the one after into registers and
+// multiplies the current one, with one barrier per step.  Plain vector loads
+// stage the slices (the direct-to-LDS path moves far fewer bytes per cycle
+// per CU).
+template <int TM, int TN>
+__global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) {
+  constexpr int MI = TM / 64;                  // 32-row products per wave (features)
+  constexpr int NJ = TN / 64;                  // 32-column products per wave (tokens)
+  constexpr int kAI = TM * 4 / (kGWaves * 64); // feature-tile transfers per wave per slice
+  constexpr int kBI = TN * 4 / (kGWaves * 64); // token-tile transfers per wave per slice
+  static_assert(kAI * kGWaves * 64 == TM * 4 && kBI * kGWaves * 64 == TN * 4, "whole tiles");
+  __shared__ GemmSmem<TM, TN> sm;
+  GemmStage<TM, TN>* stg = sm.stg;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int C = a.hidden;
+  const int width = a.width;
+  const int F = a.n_seg * width;
+  const int64_t n_tok = a.n_tok;
+  const int m0 = blockIdx.y * TM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * TN;
+  const uint64_t w_bytes = static_cast<uint64_t>(width) * C * 2;
+  const __amdgpu_buffer_rsrc_t w0 = gemm_rsrc(a.seg[0].w, w_bytes);
+  const __amdgpu_buffer_rsrc_t w1 = gemm_rsrc(a.seg[1].w, w_bytes);
+  const __amdgpu_buffer_rsrc_t w2 = gemm_rsrc(a.seg[2].w, w_bytes);
+  const __amdgpu_buffer_rsrc_t xr = gemm_rsrc(a.x, static_cast<uint64_t>(n_tok) * C * 2);
+
+  // Per-lane source offsets (bytes, at reduction offset 0) of this wave's
+  // transfers into the feature and token tiles.  A transfer covers 16 rows,
+  // all in one segment (width % 16 == 0); rows past the last segment read
+  // past their matrix and load zeros (their results are never stored).
+  uint32_t aoff[kAI], boff[kBI];
+  __amdgpu_buffer_rsrc_t arsrc[kAI];
+#pragma unroll
+  for (int u = 0; u < kAI; ++u) {
+    const int P = 64 * (wave * kAI + u) + lane;
+    const int r = P >> 2, c = (P & 3) ^ gswz(r);
+    const int fr = m0 + 16 * (wave * kAI + u);  // first row of the transfer (wave-uniform)
+    int s = fr / width;
+    s = s < a.n_seg ? s : a.n_seg - 1;
+    arsrc[u] = s == 0 ? w0 : (s == 1 ? w1 : w2);
+    const int fl = m0 + r - s * width;
+    aoff[u] = static_cast<uint32_t>((static_cast<uint64_t>(fl) * C + c * 8) * 2);
+  }
+#pragma unroll
+  for (int u = 0; u < kBI; ++u) {
+    const int P = 64 * (wave * kBI + u) + lane;
+    const int r = P >> 2, c = (P & 3) ^ gswz(r);
+    const uint64_t tkn = static_cast<uint64_t>(n0 + r);
+    // tokens past the end read past the buffer: zero
+    const uint64_t off = (tkn * C + c * 8) * 2;
+    boff[u] = off >= 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(off);
+  }
+
+  // operand read addresses (chunk units) for k-chunk 0; the k-chunk enters by XOR
+  int arow[MI], brow[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) arow[i] = wm * (TM / 2) + 32 * i + n;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) brow[j] = wn * (TN / 2) + 32 * j + n;
+
+  mfma_f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Slices go global -> registers -> LDS through kPre register buffers:
+  // step ks writes slice ks+1 (loaded kPre steps earlier) into the LDS stage
+  // that slice ks-1 was read from, reloads that register buffer with slice
+  // ks+1+kPre and multiplies slice ks.  The step loop is unrolled by kPre so
+  // that every register buffer index is static.
+  const int nk = C / kTK;
+  u32x4 R[kPre][kAI + kBI];
+  auto load_regs = [&](u32x4 (&Rb)[kAI + kBI], int k0) {
+#pragma unroll
+    for (int u = 0; u < kAI; ++u)
+      Rb[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                  arsrc[u], static_cast<int>(aoff[u] + k0 * 2), 0, 0));
+#pragma unroll
+    for (int u = 0; u < kBI; ++u)
+      Rb[kAI + u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        xr, static_cast<int>(boff[u] == 0xffffffffu ? boff[u] : boff[u] + k0 * 2), 0, 0));
+  };
+  auto store_regs = [&](const u32x4 (&Rb)[kAI + kBI], GemmStage<TM, TN>& st) {
+#pragma unroll
+    for (int u = 0; u < kAI; ++u) st.a[64 * (wave * kAI + u) + lane] = Rb[u];
+#pragma unroll
+    for (int u = 0; u < kBI; ++u) st.b[64 * (wave * kBI + u) + lane] = Rb[kAI + u];
+  };
+  // Slice s lives in register buffer s % kPre until it is written to LDS.
+  // Every load is unconditional (slices past the end reload the last one and
+  // are never multiplied), so inside the loop the compiler's load-completion
+  // waits stay exact: each step waits only for the slice it stores, not for
+  // the kPre - 1 slices loaded after it.
+  const int last = (nk - 1) * kTK;
+  load_regs(R[0], 0);
+  store_regs(R[0], stg[0]);
+#pragma unroll
+  for (int p = 1; p <= kPre; ++p) load_regs(R[p % kPre], min(p * kTK, last));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  auto multiply = [&](const GemmStage<TM, TN>& st) {
+#pragma unroll
+    for (int s = 0; s < kTK / 16; ++s) {
+      mfma_bf16x8 af[MI], bfr[NJ];
+      const int kc = 2 * s + hh;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) af[i] = as_bf16x8(st.a[arow[i] * 4 + (kc ^ gswz(arow[i]))]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bfr[j] = as_bf16x8(st.b[brow[j] * 4 + (kc ^ gswz(brow[j]))]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // Whole groups of kPre steps, no branch inside.  The store at step nk - 1
+  // (when nk % kPre == 0) writes a copy of the last slice into the stage no
+  // wave reads any more: harmless.
+  const int full = nk / kPre * kPre;
+  int kb = 0;
+  for (; kb < full; kb += kPre) {
+#pragma unroll
+    for (int p = 0; p < kPre; ++p) {
+      const int ks = kb + p;
+      store_regs(R[(p + 1) % kPre], stg[(ks + 1) & 1]);
+      load_regs(R[(p + 1) % kPre], min((ks + 1 + kPre) * kTK, last));
+      multiply(stg[ks & 1]);
+    }
+  }
+  // The last nk % kPre steps need no more loads.
+#pragma unroll
+  for (int p = 0; p + 1 < kPre; ++p) {
+    const int ks = full + p;
+    if (ks < nk) {
+      if (ks + 1 < nk) store_regs(R[(p + 1) % kPre], stg[(ks + 1) & 1]);
+      multiply(stg[ks & 1]);
+    }
+  }
+
+  // Epilogue.  acc[i][j][r]: feature m0 + wm*TM/2 + 32i + 8(r/4) + 4hh + r%4,
+  // token n0 + wn*TN/2 + 32j + n.  Key features are rotated at their token's
+  // position (4 consecutive features = 2 pairs in-lane), everything is
+  // rounded to bf16 into the LDS tile, then written out in 16-byte pieces:
+  // row-major and key rows [tok][d] directly, value rows [d][tok] gathered
+  // per feature.
+  const CacheGeom& g = a.g;
+  const int per_stream = a.frames.n * g.T;
+  asm volatile("s_barrier" ::: "memory");  // every wave is done with the stages
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int tl = wn * (TN / 2) + 32 * j + n;
+    const int64_t tkn = n0 + tl;
+    int b = 0, lf = 0, tok = 0;
+    if (a.has_key && tkn < n_tok) token_coords(tkn, per_stream, g.T, &b, &lf, &tok);
+    const int64_t t = a.has_key ? a.frames.t[lf] : 0;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int fl = wm * (TM / 2) + 32 * i + 8 * q + 4 * hh;
+        const int f = m0 + fl;  // multiple of 4
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (a.has_key && f < F) {
+          const int s = f / width;
+          if (a.seg[s].kind == kOutCacheK) {
+            const int fs = f - s * width;
+            const int head = fs / g.D, d = fs - head * g.D;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const int p = d / 2 + pp;
+              float sn, cs;
+              rope_cs(a.rope, head, p, t, tok / a.rope.grid_w, tok % a.rope.grid_w, &sn, &cs);
+              const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
+              v[2 * pp] = x0 * cs - x1 * sn;
+              v[2 * pp + 1] = x0 * sn + x1 * cs;
+            }
+          }
+        }
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(&sm.out.o[tl][fl]) = w;
+      }
+  }
+  __syncthreads();
+  uint16_t* kst = static_cast<uint16_t*>(g.k_store);
+  uint16_t* vst = static_cast<uint16_t*>(g.v_store);
+  // 16-byte pieces (token, 8 features): row-major outputs and keys
+  for (int e = threadIdx.x; e < TN * (TM / 8); e += kGWaves * 64) {
+    const int tl = e / (TM / 8), fl = (e % (TM / 8)) * 8;
+    const int64_t tkn = n0 + tl;
+    const int f = m0 + fl;
+    if (tkn >= n_tok || f >= F) continue;
+    const int s = f / width;
+    const int fs = f - s * width;
+    const u32x4 piece = *reinterpret_cast<const u32x4*>(&sm.out.o[tl][fl]);
+    if (a.seg[s].kind == kOutRows) {
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.seg[s].y) + tkn * width + fs) = piece;
+    } else if (a.seg[s].kind == kOutCacheK) {
+      int b, lf, tok;
+      token_coords(tkn, per_stream, g.T, &b, &lf, &tok);
+      const int64_t slot = a.frames.store_slot[lf];
+      const int head = fs / g.D, d = fs - head * g.D;
+      *reinterpret_cast<u32x4*>(kst + (((slot * g.B + b) * g.H + head) * g.T + tok) * g.D + d) = piece;
+    }
+  }
+  if (!a.has_value) return;
+  // 16-byte pieces (feature, 8 tokens): values
+  for (int e = threadIdx.x; e < TM * (TN / 8); e += kGWaves * 64) {
+    const int fl = e / (TN / 8), tl = (e % (TN / 8)) * 8;
+    const int f = m0 + fl;
+    const int64_t tkn0 = n0 + tl;
+    if (f >= F || tkn0 >= n_tok) continue;
+    const int s = f / width;
+    if (a.seg[s].kind != kOutCacheV) continue;
+    // 8 consecutive tokens stay in one frame and stream (T % 8 == 0)
+    int b, lf, tok;
+    token_coords(tkn0, per_stream, g.T, &b, &lf, &tok);
+    const int64_t slot = a.frames.store_slot[lf];
+    const int fv = f - s * width;
+    const int head = fv / g.D, d = fv - head * g.D;
+    uint16_t vals[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) vals[r] = sm.out.o[tl + r][fl];
+    *reinterpret_cast<u32x4*>(vst + (((slot * g.B + b) * g.H + head) * g.D + d) * g.T + tok) =
+        *reinterpret_cast<const u32x4*>(vals);
+  }
+}
+
+// fp32 path (small configurations): one thread per (token, 4 output features).
+__global__ void __launch_bounds__(256) proj_f32_kernel(ProjArgs a) {
+  const CacheGeom& g = a.g;
+  const int C = a.hidden;
+  const int width = a.width;
+  const int per_stream = a.frames.n * g.T;
+  const int64_t n_tok = a.n_tok;
+  const int quads = a.n_seg * width / 4;
+  const int64_t total = n_tok * quads;
+  const float* x = static_cast<const float*>(a.x);
+  float* kst = static_cast<float*>(g.k_store);
+  float* vst = static_cast<float*>(g.v_store);
+  for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int qd = static_cast<int>(idx % quads);
+    const int64_t tkn = idx / quads;
+    const int f = qd * 4;
+    const int s = f / width;
+    const int fs = f - s * width;
+    const ProjSeg& seg = a.seg[s];
+    const float* w = static_cast<const float*>(seg.w) + static_cast<int64_t>(fs) * C;
+    const float* xr = x + tkn * C;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < C; ++c) {
+      const float xv = xr[c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = fmaf(xv, w[static_cast<int64_t>(r) * C + c], v[r]);
+    }
+    if (seg.kind == kOutRows) {
+      float* dst = static_cast<float*>(seg.y) + tkn * width + fs;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[r] = v[r];
+      continue;
+    }
+    int b, lf, tok;
+    token_coords(tkn, per_stream, g.T, &b, &lf, &tok);
+    const int64_t slot = a.frames.store_slot[lf];
+    const int head = fs / g.D, d = fs - head * g.D;
+    if (seg.kind == kOutCacheK) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int p = d / 2 + pp;
+        float sn, cs;
+        rope_cs(a.rope, head, p, a.frames.t[lf], tok / a.rope.grid_w, tok % a.rope.grid_w, &sn, &cs);
+        const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
+        v[2 * pp] = x0 * cs - x1 * sn;
+        v[2 * pp + 1] = x0 * sn + x1 * cs;
+      }
+      float* dst = kst + (((slot * g.B + b) * g.H + head) * g.T + tok) * g.D + d;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[r] = v[r];
+    } else {
+      const int64_t base = ((slot * g.B + b) * g.H + head) * static_cast<int64_t>(g.D);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vst[(base + d + r) * g.T + tok] = v[r];
+    }
+  }
+}
+
+template <int TM, int TN>
+void launch_tile(const ProjArgs& a, hipStream_t stream) {
+  const int F = a.n_seg * a.width;
+  const dim3 grid(static_cast<unsigned>((a.n_tok + TN - 1) / TN), static_cast<unsigned>((F + TM - 1) / TM));
+  hipLaunchKernelGGL((proj_bf16_kernel<TM, TN>), grid, dim3(kGWaves * 64), 0, stream, a);
+}
+
+int64_t tiles_of(int64_t n_tok, int F, int TM, int TN) { return ((n_tok + TN - 1) / TN) * ((F + TM - 1) / TM); }
+
+}  // namespace
+
+int proj_tile_shape(int64_t n_tok, int F, int num_cus) {
+  if (const char* e = std::getenv("SA_PROJ_TILE")) {
+    const int v = std::atoi(e);
+    if (v >= 0 && v <= 2) return v;
+  }
+  // the largest tile that still gives every CU a workgroup
+  if (tiles_of(n_tok, F, 256, 128) >= num_cus) return 0;
+  if (tiles_of(n_tok, F, 128, 128) >= num_cus) return 1;
+  return 2;
+}
+
+hipError_t launch_proj(const ProjArgs& a, int dtype, int num_cus, hipStream_t stream) {
+  if (a.n_tok == 0) return hipSuccess;
+  const int F = a.n_seg * a.width;
+  if (dtype == kBF16) {
+    switch (proj_tile_shape(a.n_tok, F, num_cus)) {
+      case 0: launch_tile<256, 128>(a, stream); break;
+      case 1: launch_tile<128, 128>(a, stream); break;
+      default: launch_tile<128, 64>(a, stream); break;
+    }
+  } else {
+    const int64_t work = a.n_tok * (F / 4);
+    int64_t blocks = (work + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(proj_f32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -122,3 +122,20 @@ def test_cache_plan_rejections_and_reset(plan_harness):
     rows = _run_plan(plan_harness, 3, 9, ["a 3 0", "a 10 3", "a 1 2", "a 0 9", "a 9 3", "r", "a 1 0"])
     assert [r[0] for r in rows] == [0, 2, 3, 1, 0, 0, 0]
     assert rows[4][1] == 12 and rows[5][1] == 0 and rows[6][2] == [(0, 0, 0, 0)]
+
+
+def test_host_projection_validation():
+    """Argument checks of sa_linear / sa_cache_project_append that fail before any launch."""
+    L = _swk().lib()
+    P, Q, R = 0x100000, 0x200000, 0x300000   # 16-byte aligned stand-ins; no call below reaches the GPU
+    assert L.sa_linear(None, Q, R, 0, 4, 64, 64, None) == _swk().SA_ERR_NULL
+    assert L.sa_linear(P, Q, R + 8, 0, 4, 64, 64, None) == _swk().SA_ERR_ALIGN
+    assert L.sa_linear(P, Q, R, 7, 4, 64, 64, None) == _swk().SA_ERR_DTYPE
+    assert L.sa_linear(P, Q, R, 0, 4, 48, 64, None) == _swk().SA_ERR_SHAPE     # in % 32
+    assert L.sa_linear(P, Q, R, 0, 4, 64, 24, None) == _swk().SA_ERR_SHAPE     # out % 16
+    assert L.sa_linear(P, Q, R, 0, -1, 64, 64, None) == _swk().SA_ERR_SHAPE
+    assert L.sa_linear(P, Q, R, 0, 1 << 26, 64, 64, None) == _swk().SA_ERR_SHAPE   # x reaches 4 GiB
+    assert L.sa_linear(P, Q, P + 256, 0, 4, 64, 64, None) == _swk().SA_ERR_RANGE   # y overlaps x
+    assert L.sa_linear(P, Q, Q, 0, 4, 64, 64, None) == _swk().SA_ERR_RANGE         # y overlaps w
+    assert L.sa_linear(P, Q, R, 0, 0, 64, 64, None) == _swk().SA_OK                # nothing to do
+    assert L.sa_cache_project_append(None, P, None, Q, R, 64, None, 1, 0, None) == _swk().SA_ERR_NULL

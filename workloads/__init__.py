@@ -25,7 +25,7 @@ from typing import Tuple
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_X, TENSOR_WK, TENSOR_WV, TENSOR_EPS = range(7)
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_X, TENSOR_WK, TENSOR_WV, TENSOR_EPS, TENSOR_WQ, TENSOR_WO, TENSOR_XF = range(10)
 
 
 @dataclass(frozen=True)
@@ -137,3 +137,28 @@ def recache_inputs(w: Workload, layer: int = 0, n_frames: int | None = None, bas
     wk = normal((C, HD), w.cfg, layer, 0, 0, TENSOR_WK, 1.0 / np.sqrt(C), w.dtype, base)
     wv = normal((C, HD), w.cfg, layer, 0, 0, TENSOR_WV, 1.0 / np.sqrt(C), w.dtype, base)
     return x, wk, wv
+
+
+def frame_hidden(w: Workload, first_frame: int, n_frames: int = 1, layer: int = 0, base: int = 0) -> np.ndarray:
+    """Hidden states of frames first_frame.. (one seed per frame and stream): [B, n*T_f, C] ~ N(0,1)."""
+    T = w.tokens_per_frame
+    x = np.empty((w.batch, n_frames * T, w.hidden), dtype=np.float32)
+    for b in range(w.batch):
+        for j in range(n_frames):
+            x[b, j * T:(j + 1) * T] = normal((T, w.hidden), w.cfg, layer, b, first_frame + j, TENSOR_XF, 1.0,
+                                             w.dtype, base)
+    return x
+
+
+def projection_weights(w: Workload, layer: int = 0, base: int = 0):
+    """W_q, W_k, W_v [C, H*D] ~ N(0, 1/C) (x . W orientation), fixed per layer."""
+    C, HD = w.hidden, w.n_heads * w.head_dim
+    return tuple(normal((C, HD), w.cfg, layer, 0, 1, t, 1.0 / np.sqrt(C), w.dtype, base)
+                 for t in (TENSOR_WQ, TENSOR_WK, TENSOR_WV))
+
+
+def output_weight(w: Workload, out_features: int | None = None, layer: int = 0, base: int = 0) -> np.ndarray:
+    """W_o [H*D, out] ~ N(0, 1/(H*D)) (x . W orientation); out defaults to the model width C."""
+    HD = w.n_heads * w.head_dim
+    out = w.hidden if out_features is None else out_features
+    return normal((HD, out), w.cfg, layer, 0, 1, TENSOR_WO, 1.0 / np.sqrt(HD), w.dtype, base)
