@@ -24,6 +24,9 @@ float64, written from the pages:
                    appended to the cache, and a plain linear map x W
                    (LoL paper review, background "multi-head attention";
                    LongLive paper review, section 3 "KV Recache").
+* ``diagnostics`` -- per-head softmax mass on the sink frames and the
+                   phase-coherence kernel C(Delta) (LoL paper review, "core
+                   method" and "core innovation" paragraphs).
 * ``brute``     -- pure-Python loop versions for tiny shapes, used to pin the
                    numpy versions.
 * ``stream``    -- composes the above into the per-frame stream the library
@@ -32,4 +35,4 @@ float64, written from the pages:
 Pins (tests/test_oracle_*.py) tie these to closed forms, invariants,
 library routines and brute force; see the test docstrings.
 """
-from . import rope, cache, attention, recache, project, brute, stream  # noqa: F401
+from . import rope, cache, attention, recache, project, brute, stream, diagnostics  # noqa: F401

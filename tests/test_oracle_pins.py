@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from oracle import attention as oattn
-from oracle import brute, cache as ocache, project as oproject, recache as orecache, rope as orope, stream as ostream
+from oracle import brute, cache as ocache, diagnostics as odiag, project as oproject, recache as orecache, rope as orope, stream as ostream
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(1234)
@@ -335,6 +335,80 @@ def test_p9_project_append_brute_force():
                 ref = brute.rope_vector(kb[row][h * D:(h + 1) * D], brute.positions(t0 + j, tok, grid[1], dims),
                                         brute.frequencies(bases[h], dims))
                 np.testing.assert_allclose(kf[0, tok, h], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ P10 LoL diagnostics
+@pytest.mark.parametrize("causal", [True, False])
+def test_p10_sink_mass_brute_force(causal):
+    """Sink mass = the brute-force attention row of 0/1 values marking the sink keys (pure-Python loops)."""
+    bases, dims, grid = _tiny_setup()
+    T, H, D = 4, 2, 8
+    so = ostream.StreamOracle(2, 2, T, grid[1], dims, bases)
+    for f in range(6):
+        so.append(RNG.standard_normal((1, T, H, D)), RNG.standard_normal((1, T, H, D)), 3 + f)
+    q = RNG.standard_normal((1, 2 * T, H, D)) * 2.0
+    mass = odiag.sink_mass(so, q, causal)
+    res = so.resident()
+    qframes = res[-2:]
+    for i, fq in enumerate(qframes):
+        for tok in range(T):
+            for h in range(H):
+                qv = brute.rope_vector(q[0, i * T + tok, h].tolist(),
+                                       brute.positions(so.model.t[fq], tok, grid[1], dims),
+                                       brute.frequencies(bases[h], dims))
+                keys, marks = [], []
+                for fk in res:
+                    if causal and fk > fq:
+                        continue
+                    for kt in range(T):
+                        keys.append(so.frame_kv(fk)[0][0, kt, h].tolist())
+                        marks.append([1.0 if fk < 2 else 0.0])
+                ref = brute.attention_row(qv, keys, marks, 1.0 / math.sqrt(D))[0]
+                assert abs(mass[0, i * T + tok, h] - ref) <= 1e-12
+
+
+def test_p10_sink_mass_closed_forms():
+    """No sinks -> 0; a query frame that is itself a sink sees only sinks -> 1; q = 0 -> the share of
+    visible sink keys."""
+    bases, dims, grid = _tiny_setup()
+    T, H, D = 4, 2, 8
+    none = ostream.StreamOracle(0, 3, T, grid[1], dims, bases)
+    both = ostream.StreamOracle(2, 3, T, grid[1], dims, bases)
+    for f in range(5):
+        k, v = RNG.standard_normal((1, T, H, D)), RNG.standard_normal((1, T, H, D))
+        none.append(k, v, f)
+        both.append(k, v, f)
+        q = RNG.standard_normal((1, T, H, D))
+        assert np.all(odiag.sink_mass(none, q, True) == 0.0)
+        m = odiag.sink_mass(both, q, True)
+        if f < 2:
+            np.testing.assert_allclose(m, 1.0, rtol=0, atol=1e-15)
+        visible = len(both.resident())
+        np.testing.assert_allclose(odiag.sink_mass(both, np.zeros_like(q), True), min(f + 1, 2) / visible,
+                                   rtol=0, atol=1e-15)
+
+
+def test_p10_phase_coherence():
+    """C(0) = 1; |C| <= 1; sigma = 0 -> every head equal; d_t = 2 -> C = exp(j Delta) (w_0 = 1);
+    brute-force cos/sin loops over the time frequencies."""
+    deltas = [0, 1, 3, 132, 201, 1200]
+    eps = RNG.uniform(-1, 1, size=4)
+    bases = orope.theta_hat(10000.0, 0.8, eps)
+    dims = (44, 42, 42)
+    c = odiag.phase_coherence(bases, dims, deltas)
+    np.testing.assert_allclose(c[:, 0], 1.0, atol=1e-15)
+    assert np.all(np.abs(c) <= 1.0 + 1e-12)
+    assert np.abs(c[0] - c[1]).max() > 1e-3          # jitter separates the heads
+    flat = odiag.phase_coherence(orope.theta_hat(10000.0, 0.0, eps), dims, deltas)
+    np.testing.assert_allclose(flat, np.broadcast_to(flat[0], flat.shape), rtol=0, atol=0)
+    one = odiag.phase_coherence(bases, (2, 4, 2), deltas)
+    np.testing.assert_allclose(one, np.exp(1j * np.array(deltas, dtype=float))[None, :].repeat(4, 0), atol=1e-12)
+    for h in range(4):
+        w = brute.frequencies(bases[h], dims)[:dims[0] // 2]
+        for n, dl in enumerate(deltas):
+            re = sum(math.cos(x * dl) for x in w) / len(w)
+            im = sum(math.sin(x * dl) for x in w) / len(w)
+            assert abs(c[h, n].real - re) <= 1e-12 and abs(c[h, n].imag - im) <= 1e-12
 
 
 # ------------------------------------------------------------ P7 closed forms
