@@ -220,6 +220,20 @@ def main():
     print(f"[bench] step {ms_per_step * 1e3:.1f} us, attention {att_avg * 1e3:.1f} us "
           f"({achieved:.0f} TFLOP/s), append {app_avg * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # LoL diagnostic: the same attention call also reporting each row's
+    # softmax mass on the sink frames (a second pass over the sink keys).
+    mass = torch.empty((1, T, H), dtype=torch.float32, device=dev)
+    c0 = caches[0]
+    for _ in range(3):
+        swk.sa_window_attn_sink_mass(c0, qs[0], o, mass, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+    em0, em1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    em0.record(stream)
+    for _ in range(20):
+        swk.sa_window_attn_sink_mass(c0, qs[0], o, mass, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+    em1.record(stream)
+    torch.cuda.synchronize()
+    mass_us = em0.elapsed_time(em1) * 1e3 / 20
+
     # Standalone RoPE (Q of one frame, read + write) and the KV recache.
     qrot = torch.empty_like(qs[0])
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -250,6 +264,49 @@ def main():
     rc_us = e0.elapsed_time(e1) * 1e3 / n_rc
     rc_flops = 2.0 * (n_win * T) * (2 * H * D) * w4.hidden
     rc_bytes = (n_win * T * w4.hidden + 2 * H * D * w4.hidden + 2 * n_win * T * H * D) * 2
+
+    # One layer's self-attention block per frame, hidden 1536: fused Q/K/V
+    # projections with RoPE and the append, the attention, and the output
+    # projection (seeded random weights of that shape; no model).
+    C = w4.hidden
+    HD = H * D
+    wq_, wk_, wv_ = wl.projection_weights(w4)
+    dqw, dkw, dvw = (torch.from_numpy(np.ascontiguousarray(m.T)).to(dev, bf).contiguous() for m in (wq_, wk_, wv_))
+    dow = torch.from_numpy(np.ascontiguousarray(wl.output_weight(w4).T)).to(dev, bf).contiguous()
+    xs = [torch.from_numpy(wl.frame_hidden(w4, f, 1)).to(dev, bf).contiguous() for f in range(4)]
+    cb = swk.Cache(rope, 1, w.n_sink, w.n_local, bf, device=dev)
+    qb = torch.empty((1, T, H, D), dtype=bf, device=dev)
+    ob = torch.empty_like(qb)
+    yb = torch.empty((T, C), dtype=bf, device=dev)
+    tb = 0
+    for f in range(n_win):
+        swk.sa_cache_project_append(cb, xs[f % 4], dqw, dkw, dvw, C, qb, 1, tb)
+        tb += 1
+    # back to back, one synchronisation at the end (events between the launches)
+    n_blk, n_skip = 43, 3
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_blk)]
+    for it in range(n_blk):
+        ea, eb, ec, ed = bev[it]
+        ea.record(stream)
+        swk.sa_cache_project_append(cb, xs[it % 4], dqw, dkw, dvw, C, qb, 1, tb)
+        eb.record(stream)
+        swk.sa_window_attn(cb, qb, ob, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+        ec.record(stream)
+        swk.sa_linear(ob, dow, yb, T, HD, C)
+        ed.record(stream)
+        tb += 1
+    torch.cuda.synchronize()
+    pj_ms = [e[0].elapsed_time(e[1]) for e in bev[n_skip:]]
+    ab_ms = [e[1].elapsed_time(e[2]) for e in bev[n_skip:]]
+    op_ms = [e[2].elapsed_time(e[3]) for e in bev[n_skip:]]
+    pj_avg, ab_avg, op_avg = (sum(v) / len(v) for v in (pj_ms, ab_ms, op_ms))
+    pj_flops = 2.0 * T * C * 3 * HD
+    op_flops = 2.0 * T * HD * C
+    print(f"[bench] layer block: q/k/v projection + append {pj_avg * 1e3:.1f} us "
+          f"({pj_flops / (pj_avg * 1e-3) / 1e12:.0f} TFLOP/s), attention {ab_avg * 1e3:.1f} us, "
+          f"output projection {op_avg * 1e3:.1f} us ({op_flops / (op_avg * 1e-3) / 1e12:.0f} TFLOP/s)",
+          file=sys.stderr, flush=True)
+    cb.close()
 
     # Chunked, batched shape: B = 4 streams, 3-frame query chunks, frame-causal
     # (4680 queries per stream over 10/11/12 visible frames), sigma = 0.8.
@@ -323,12 +380,25 @@ def main():
                      "median_launch_us": round(att_ms[len(att_ms) // 2] * 1e3, 2)},
         "append": {"avg_us": round(app_avg * 1e3, 2), "bytes": append_bytes,
                    "GBps": round(append_bytes / (app_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBPS},
+        "sink_mass": {"avg_us": round(mass_us, 1),
+                      "vs_attention_only": round(mass_us / (att_avg * 1e3), 3),
+                      "note": "sa_window_attn_sink_mass: the attention plus each row's softmax mass on the "
+                              "3 sink frames, per head"},
         "rope3d_q": {"avg_us": round(rope_us, 2), "bytes": rope_bytes,
                      "GBps": round(rope_bytes / (rope_us * 1e-6) / 1e9, 1)},
         "recache": {"avg_us": round(rc_us, 1), "flops": rc_flops,
                     "TFLOPs": round(rc_flops / (rc_us * 1e-6) / 1e12, 1),
                     "pct_bf16_peak": round(100.0 * rc_flops / (rc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
                     "min_bytes": rc_bytes},
+        "layer_block": {"workload": "wan13b self-attention block per frame: x [1560 x 1536] -> fused q/k/v "
+                                     "projections + RoPE + append, attention over 12 frames, output projection "
+                                     "[1560 x 1536] . [1536 x 1536]",
+                        "qkv_append_avg_us": round(pj_avg * 1e3, 1), "qkv_flops": pj_flops,
+                        "qkv_TFLOPs": round(pj_flops / (pj_avg * 1e-3) / 1e12, 1),
+                        "attention_avg_us": round(ab_avg * 1e3, 1),
+                        "out_proj_avg_us": round(op_avg * 1e3, 1), "out_proj_flops": op_flops,
+                        "out_proj_TFLOPs": round(op_flops / (op_avg * 1e-3) / 1e12, 1),
+                        "latent_frames_per_s_per_layer": round(1e3 / (pj_avg + ab_avg + op_avg), 1)},
         "chunked_b4": {"workload": "wan13b-chunk3-b4: B=4, 3-frame query chunks (4680 queries per stream), "
                                     "frame-causal over 10/11/12 visible frames, sigma=0.8, one layer",
                        "attention_avg_us": round(a5_avg * 1e3, 1), "flops": flops5,

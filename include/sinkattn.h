@@ -230,6 +230,28 @@ sa_status sa_window_attn_workspace(const sa_cache* cache, int32_t n_q, size_t* b
 sa_status sa_window_attn(const sa_cache* cache, const void* q, void* o, int32_t n_q, float scale,
                          sa_mask mask, void* workspace, size_t workspace_bytes, void* stream);
 
+/* LoL collapse diagnostic ([LoL] "core method" paragraph: at a sink collapse
+ * several heads at once put abnormally high attention weight on the sink
+ * frames).  Same arguments, workspace and output o as sa_window_attn, plus
+ *   sink_mass [B, n_q*T_f, H] fp32: for each query row and head, the softmax
+ *             probability mass the row puts on the keys of the resident sink
+ *             frames (0 when no sink frame is resident).
+ * It runs the attention, which also records each row's log-sum-exp, then the
+ * same rows over the sink keys only (about n_sink / (n_sink + n_local) of the
+ * attention's work); mass = exp(LSE_sinks - LSE_all). */
+sa_status sa_window_attn_sink_mass(const sa_cache* cache, const void* q, void* o, float* sink_mass,
+                                   int32_t n_q, float scale, sa_mask mask, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Phase-coherence kernel per head ([LoL] "core innovation" paragraph), on the
+ * host in fp64, from the same tables sa_rope_create builds:
+ *   C_h(delta) = (1/K) sum_{i<K} exp(j w_{h,t,i} delta)
+ * over head h's K = dim_t/2 time-axis frequencies, delta a frame offset.
+ *   deltas [n] host; re, im [n_heads][n] host.  No HIP call.
+ * SA_ERR_SHAPE if dim_t is 0. */
+sa_status sa_rope_phase_coherence(const sa_rope_desc* desc, const double* deltas, int32_t n, double* re,
+                                  double* im);
+
 /* Resident frames in logical order (host, no sync): writes min(cap, n) entries,
  * *n_valid = n. */
 sa_status sa_cache_slots(const sa_cache* cache, sa_slot* out, int32_t cap, int32_t* n_valid);

@@ -69,6 +69,11 @@ _SIGNATURES = {
     "sa_cache_project_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, ctypes.c_int32,
                                                ctypes.c_int64, _VP]),
     "sa_linear": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _VP]),
+    "sa_window_attn_sink_mass": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
+                                                _VP, ctypes.c_size_t, _VP]),
+    "sa_rope_phase_coherence": (ctypes.c_int, [ctypes.POINTER(sa_rope_desc), ctypes.POINTER(ctypes.c_double),
+                                               ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
+                                               ctypes.POINTER(ctypes.c_double)]),
     "sa_window_attn_workspace": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "sa_window_attn": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _VP,
                                       ctypes.c_size_t, _VP]),
@@ -267,6 +272,26 @@ def sa_window_attn(cache: Cache, q, o, n_q: int, scale: float = 0.0, mask: int =
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sa_window_attn(cache.handle, _ptr(q), _ptr(o), n_q, scale, mask, _ptr(workspace),
                                 ws_bytes, _stream(stream)), "sa_window_attn")
+
+
+def sa_window_attn_sink_mass(cache: Cache, q, o, sink_mass, n_q: int, scale: float = 0.0,
+                             mask: int = SA_MASK_NONE, workspace=None, stream=None):
+    """o as sa_window_attn; sink_mass [B, n_q*T_f, H] float32 = softmax mass on the sink-frame keys."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().sa_window_attn_sink_mass(cache.handle, _ptr(q), _ptr(o), _ptr(sink_mass), n_q, scale, mask,
+                                          _ptr(workspace), ws_bytes, _stream(stream)), "sa_window_attn_sink_mass")
+
+
+def sa_rope_phase_coherence(n_heads, head_dim, dims, grid, deltas: Sequence[float], theta0=10000.0, sigma=0.0,
+                            eps=None, jitter_axes=SA_AXIS_T):
+    """Host-only C_h(delta) over each head's time-axis frequencies: list (per head) of complex values."""
+    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes)
+    n = len(deltas)
+    dl = (ctypes.c_double * max(n, 1))(*[float(x) for x in deltas])
+    re = (ctypes.c_double * max(n_heads * n, 1))()
+    im = (ctypes.c_double * max(n_heads * n, 1))()
+    _check(lib().sa_rope_phase_coherence(ctypes.byref(d), dl, n, re, im), "sa_rope_phase_coherence")
+    return [[complex(re[h * n + k], im[h * n + k]) for k in range(n)] for h in range(n_heads)]
 
 
 def sa_cache_slots(cache: Cache) -> List[sa_slot]:

@@ -5,6 +5,7 @@
 // thread-local last-error string says why.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -224,6 +225,30 @@ sa_status sa_rope_tables(const sa_rope_desc* desc, double* theta_hat_out, double
   return ok();
 }
 
+sa_status sa_rope_phase_coherence(const sa_rope_desc* desc, const double* deltas, int32_t n, double* re,
+                                  double* im) {
+  if (sa_status s = check_rope_desc(desc)) return s;
+  if (n < 0 || (n > 0 && (!deltas || !re || !im))) return fail(SA_ERR_NULL, "deltas, re and im must be non-NULL");
+  if (desc->dim_t == 0) return fail(SA_ERR_SHAPE, "no time-axis channels (dim_t is 0)");
+  const int dims[3] = {desc->dim_t, desc->dim_h, desc->dim_w};
+  const sa::RopeTables t = sa::build_rope_tables(desc->n_heads, desc->head_dim, dims, desc->theta0,
+                                                 desc->sigma, desc->eps, desc->jitter_axes);
+  const int half = desc->head_dim / 2;
+  const int K = desc->dim_t / 2;  // time pairs come first in every head's table
+  for (int h = 0; h < desc->n_heads; ++h)
+    for (int k = 0; k < n; ++k) {
+      double c = 0.0, s = 0.0;
+      for (int i = 0; i < K; ++i) {
+        const double ph = t.freq[static_cast<size_t>(h) * half + i] * deltas[k];
+        c += std::cos(ph);
+        s += std::sin(ph);
+      }
+      re[static_cast<size_t>(h) * n + k] = c / K;
+      im[static_cast<size_t>(h) * n + k] = s / K;
+    }
+  return ok();
+}
+
 sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out) {
   if (!out) return fail(SA_ERR_NULL, "out is NULL");
   if (sa_status s = check_rope_desc(desc)) return s;
@@ -434,8 +459,12 @@ sa_status sa_window_attn_workspace(const sa_cache* c, int32_t n_q, size_t* bytes
   return ok();
 }
 
-sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q, float scale, sa_mask mask,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sa_status check_attn(const sa_cache* c, const void* q, void* o, int32_t n_q, float scale, sa_mask mask,
+                     void* workspace, size_t workspace_bytes) {
   if (!c || !q || !o) return fail(SA_ERR_NULL, "cache, q and o must be non-NULL");
   if (!aligned16(q) || !aligned16(o) || !aligned16(workspace)) return fail(SA_ERR_ALIGN, "q, o and workspace must be 16-byte aligned");
   if (q == o) return fail(SA_ERR_RANGE, "o must not alias q");
@@ -446,6 +475,14 @@ sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q,
   if (sa_status s = attn_plan(c, n_q, &splits, &need)) return s;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SA_ERR_RANGE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  return SA_OK;
+}
+
+sa::AttnArgs attn_args(const sa_cache* c, const void* q, void* o, int32_t n_q, float scale, sa_mask mask,
+                       void* workspace) {
+  int splits = 1;
+  size_t need = 0;
+  (void)attn_plan(c, n_q, &splits, &need);
   sa::AttnArgs a;
   a.q = q;
   a.o = o;
@@ -461,8 +498,55 @@ sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q,
   a.store_bytes = static_cast<uint32_t>(sa_cache_store_bytes(&c->desc));
   a.n_waves = sa::attn_waves(c->desc.dtype, c->desc.batch, c->desc.n_heads, c->desc.head_dim,
                              c->desc.tokens_per_frame, n_q, device_cus());
+  a.key_limit = INT32_MAX;
+  a.stat_mode = sa::kStatNone;
+  a.stat = nullptr;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q, float scale, sa_mask mask,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (sa_status s = check_attn(c, q, o, n_q, scale, mask, workspace, workspace_bytes)) return s;
+  const sa::AttnArgs a = attn_args(c, q, o, n_q, scale, mask, workspace);
   const hipError_t e = sa::launch_window_attn(a, c->desc.dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+sa_status sa_window_attn_sink_mass(const sa_cache* c, const void* q, void* o, float* sink_mass, int32_t n_q,
+                                   float scale, sa_mask mask, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!sink_mass) return fail(SA_ERR_NULL, "sink_mass must be non-NULL");
+  if (!aligned16(sink_mass)) return fail(SA_ERR_ALIGN, "sink_mass must be 16-byte aligned");
+  if (sa_status s = check_attn(c, q, o, n_q, scale, mask, workspace, workspace_bytes)) return s;
+  sa::AttnArgs a = attn_args(c, q, o, n_q, scale, mask, workspace);
+  int n_sink_res = 0;
+  for (const auto& f : c->plan.resident()) n_sink_res += f.segment == 0 ? 1 : 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // pass 1: the attention itself, plus each row's log2-sum-exp2 (or 0 when no sink is resident)
+  a.stat_mode = n_sink_res > 0 ? sa::kStatLse : sa::kStatZero;
+  a.stat = sink_mass;
+  hipError_t e = sa::launch_window_attn(a, c->desc.dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (n_sink_res > 0) {
+    // pass 2: the same rows over the sink keys only (the first n_sink_res
+    // resident frames); the mass is 2^(LSE_sink - LSE_all).  At most as many
+    // key splits as the shortest row has key tiles, so no split is empty.
+    const int T = c->desc.tokens_per_frame;
+    const int n_res = static_cast<int>(c->plan.resident().size());
+    a.key_limit = n_sink_res * T;
+    const int shortest = mask == SA_MASK_FRAME_CAUSAL ? (n_res - n_q + 1) * T : n_res * T;
+    const int min_tiles = (std::min(shortest, a.key_limit) + 63) / 64;
+    a.n_splits = std::max(1, std::min(a.n_splits, min_tiles));
+    a.o = nullptr;
+    a.stat_mode = sa::kStatMass;
+    e = sa::launch_window_attn(a, c->desc.dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "sink-mass launch");
+  }
   return ok();
 }
 

@@ -52,7 +52,15 @@ struct AttnArgs {
   float* ws;          // split partials, see attn_workspace_bytes
   uint32_t store_bytes;  // bytes of each cache store (< 4 GiB)
   int32_t n_waves;       // waves per workgroup (bf16 kernel)
+  int32_t key_limit;     // keys at logical index >= key_limit are hidden (INT32_MAX: none)
+  // Per-row statistic, stat[(b*Lq + row)*H + h] (fp32):
+  //   kStatNone: not written; kStatLse: the row's log2-sum-exp2 of its scaled
+  //   scores; kStatMass: 2^(this call's log2-sum-exp2 - stat), o not written;
+  //   kStatZero: 0.
+  int32_t stat_mode;
+  float* stat;
 };
+enum AttnStat : int { kStatNone = 0, kStatLse = 1, kStatMass = 2, kStatZero = 3 };
 
 // Projection GEMM: out[n][f] = sum_c x[n][c] W[f][c] over up to three
 // output segments of `width` features each (one weight matrix per segment).

@@ -72,6 +72,15 @@ __device__ __forceinline__ int key_perm(int m) {  // swap bits 2 and 3
 
 __device__ __forceinline__ mfma_bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(mfma_bf16x8, v); }
 
+// Per-row statistic from a row's final (m, l) in the exp2 domain: the
+// log2-sum-exp2 of its scaled scores is m + log2(l).
+__device__ __forceinline__ void write_stat(int mode, float* dst, float m, float l) {
+  const float lse = m + log2f(l);
+  if (mode == kStatLse) *dst = lse;
+  else if (mode == kStatMass) *dst = exp2f(lse - *dst);
+  else *dst = 0.f;
+}
+
 // Two fp32 -> packed bf16x2 with the hardware converter (round to nearest even).
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   const f32x2_t v = {lo, hi};
@@ -215,14 +224,15 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   const int row = qt * kQTile + wave * kQW + n;
   const bool row_ok = row < Lq;
   const int qf = row_ok ? row / T : a.n_q - 1;
-  const int kend = a.causal ? (first_q + qf + 1) * T : n_keys;
+  const int klim = min(n_keys, a.key_limit);
+  const int kend = min(a.causal ? (first_q + qf + 1) * T : n_keys, klim);
   const int wave_row0 = qt * kQTile + wave_u * kQW;  // wave-uniform (scalar) from here on
   const bool wave_active = wave_row0 < Lq;
   const int wave_last = min(wave_row0 + kQW - 1, Lq - 1);
-  const int wave_kend = a.causal ? (first_q + wave_last / T + 1) * T : n_keys;            // largest kend
-  const int wave_kmin = a.causal ? (first_q + min(wave_row0, Lq - 1) / T + 1) * T : n_keys;  // smallest
+  const int wave_kend = min(a.causal ? (first_q + wave_last / T + 1) * T : n_keys, klim);            // largest kend
+  const int wave_kmin = min(a.causal ? (first_q + min(wave_row0, Lq - 1) / T + 1) * T : n_keys, klim);  // smallest
   const int last_row = min(qt * kQTile + kQTile - 1, Lq - 1);
-  const int kend_wg = a.causal ? (first_q + last_row / T + 1) * T : n_keys;
+  const int kend_wg = min(a.causal ? (first_q + last_row / T + 1) * T : n_keys, klim);
   const int n_tiles = (kend_wg + kKTile - 1) / kKTile;
   const int tile_lo = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / a.n_splits);
   const int tile_hi = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / a.n_splits);
@@ -489,13 +499,15 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
       const int64_t plane = static_cast<int64_t>(g.B) * g.H * Lq;
       const int64_t prow = static_cast<int64_t>(bh) * Lq + row;
       float* po = a.ws + (split * plane + prow) * D;
+      if (a.stat_mode != kStatMass) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 w = {oacc[db][4 * gq], oacc[db][4 * gq + 1], oacc[db][4 * gq + 2], oacc[db][4 * gq + 3]};
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
-        }
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x4 w = {oacc[db][4 * gq], oacc[db][4 * gq + 1], oacc[db][4 * gq + 2], oacc[db][4 * gq + 3]};
+            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
+          }
+      }
       if (hh == 0) {
         float* pml = a.ws + static_cast<int64_t>(a.n_splits) * plane * D + (split * plane + prow) * 2;
         pml[0] = m_run;
@@ -504,7 +516,9 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
     }
     return;
   }
-  if (row_ok) {
+  if (row_ok && a.stat_mode != kStatNone && hh == 0)
+    write_stat(a.stat_mode, a.stat + (static_cast<int64_t>(b) * Lq + row) * g.H + h, m_run, l_tot);
+  if (row_ok && a.stat_mode != kStatMass) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
 #pragma unroll
@@ -527,7 +541,8 @@ constexpr int kF32Keys = 32;
 // M = max_s m_s, splits in order.  16 lanes per row, 8 channels each.
 template <int D>
 __global__ void __launch_bounds__(256) attn_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ o,
-                                                         int B, int H, int Lq, int n_splits) {
+                                                         int B, int H, int Lq, int n_splits, int stat_mode,
+                                                         float* __restrict__ stat) {
   constexpr int kLanes = D / 8;
   constexpr int kRows = 256 / kLanes;
   const int64_t plane = static_cast<int64_t>(B) * H * Lq;
@@ -537,8 +552,19 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const float* __restrict
   const float* pml = ws + static_cast<int64_t>(n_splits) * plane * D;
   float M = kNegInf;
   for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, pml[(sp * plane + prow) * 2]);
+  const int64_t bh = prow / Lq;
+  const int row = static_cast<int>(prow - bh * Lq);
+  const int b = static_cast<int>(bh / H), h = static_cast<int>(bh - static_cast<int64_t>(b) * H);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
+  if (stat_mode == kStatMass) {  // statistics only: the partial O were not written
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float ms = pml[(sp * plane + prow) * 2];
+      if (ms != kNegInf) l += pml[(sp * plane + prow) * 2 + 1] * __builtin_amdgcn_exp2f(ms - M);
+    }
+    if (c8 == 0) write_stat(stat_mode, stat + (static_cast<int64_t>(b) * Lq + row) * H + h, M, l);
+    return;
+  }
   for (int sp = 0; sp < n_splits; ++sp) {
     const float ms = pml[(sp * plane + prow) * 2];
     if (ms == kNegInf) continue;
@@ -552,10 +578,9 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const float* __restrict
       acc[4 + i] += x1[i] * w;
     }
   }
+  if (stat_mode != kStatNone && c8 == 0)
+    write_stat(stat_mode, stat + (static_cast<int64_t>(b) * Lq + row) * H + h, M, l);
   const float inv = 1.f / l;
-  const int64_t bh = prow / Lq;
-  const int row = static_cast<int>(prow - bh * Lq);
-  const int b = static_cast<int>(bh / H), h = static_cast<int>(bh - static_cast<int64_t>(b) * H);
   u32x4 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = cvt_pk_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
@@ -577,9 +602,10 @@ __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
   const bool row_ok = row < Lq;
   const int qf = row_ok ? row / T : a.n_q - 1;
   const int n_keys = n_res * T;
-  const int kend = a.causal ? (first_q + qf + 1) * T : n_keys;
+  const int klim = min(n_keys, a.key_limit);
+  const int kend = min(a.causal ? (first_q + qf + 1) * T : n_keys, klim);
   const int last_row = min(static_cast<int>(blockIdx.x) * kF32Rows + kF32Rows - 1, Lq - 1);
-  const int kend_wg = a.causal ? (first_q + last_row / T + 1) * T : n_keys;
+  const int kend_wg = min(a.causal ? (first_q + last_row / T + 1) * T : n_keys, klim);
 
   float q[D];
   {
@@ -645,7 +671,9 @@ __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
       for (int d = 0; d < D; ++d) o[d] = fmaf(p, vs[r][d], o[d]);
     }
   }
-  if (row_ok) {
+  if (row_ok && a.stat_mode != kStatNone)
+    write_stat(a.stat_mode, a.stat + (static_cast<int64_t>(b) * Lq + row) * g.H + h, m_run, l_run);
+  if (row_ok && a.stat_mode != kStatMass) {
     const float inv = 1.f / l_run;
     float* orow = static_cast<float*>(a.o) + ((static_cast<int64_t>(b) * Lq + row) * g.H + h) * D;
 #pragma unroll
@@ -733,10 +761,10 @@ hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) 
       const dim3 mgrid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
       if (a.g.D == 128)
         hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, dim3(256), 0, stream, a.ws, static_cast<uint16_t*>(a.o),
-                           a.g.B, a.g.H, Lq, a.n_splits);
+                           a.g.B, a.g.H, Lq, a.n_splits, a.stat_mode, a.stat);
       else
         hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, dim3(256), 0, stream, a.ws, static_cast<uint16_t*>(a.o),
-                           a.g.B, a.g.H, Lq, a.n_splits);
+                           a.g.B, a.g.H, Lq, a.n_splits, a.stat_mode, a.stat);
     }
   } else {
     const dim3 grid((Lq + kF32Rows - 1) / kF32Rows, BH, 1);

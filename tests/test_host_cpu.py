@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import cache as ocache
+from oracle import diagnostics as odiag
 from oracle import rope as orope
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -45,6 +46,22 @@ def test_host_rope_tables_match_oracle(sigma, axes, names):
     np.testing.assert_allclose(np.array(th), bases, rtol=1e-15)
     for h in range(12):
         np.testing.assert_allclose(fr[h], orope.head_frequencies(bases[h], (44, 42, 42)), rtol=1e-14)
+
+
+@pytest.mark.parametrize("sigma,axes,names,dims", [(0.8, 1, ("t",), (44, 42, 42)), (0.0, 1, ("t",), (44, 42, 42)),
+                                                   (0.8, 7, ("t", "h", "w"), (22, 22, 20))])
+def test_host_phase_coherence_matches_oracle(sigma, axes, names, dims):
+    """The library's host C_h(delta) over each head's time frequencies equals the oracle's."""
+    swk = _swk()
+    D = sum(dims)
+    eps = np.random.default_rng(5).uniform(-1, 1, 12)
+    deltas = [0, 1, 2, 3, 11, 132, 201, 1200, -7]
+    got = np.array(swk.sa_rope_phase_coherence(12, D, dims, (30, 52), deltas, 10000.0, sigma, eps, axes))
+    ref = odiag.phase_coherence(orope.theta_hat(10000.0, sigma, eps, jitter_axes=names), dims, deltas)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    with pytest.raises(swk.SinkAttnError) as e:
+        swk.sa_rope_phase_coherence(12, 128, (0, 64, 64), (30, 52), deltas)
+    assert e.value.status == swk.SA_ERR_SHAPE
 
 
 @pytest.mark.parametrize("kw,status", [
