@@ -234,6 +234,28 @@ def main():
     torch.cuda.synchronize()
     mass_us = em0.elapsed_time(em1) * 1e3 / 20
 
+    # Window-size variants (3, 12 and 24 local frames without sinks; 9 local
+    # + 3 sink is the main workload): steady-state attention of one frame.
+    windows = {}
+    for n_s, n_l in ((0, 3), (0, 12), (0, 24)):
+        cw = swk.Cache(rope, 1, n_s, n_l, bf, device=dev)
+        for f in range(n_s + n_l):
+            swk.sa_cache_append(cw, ks[f % pool], vs[f % pool], 1, f)
+        wsw = torch.zeros(max(swk.sa_window_attn_workspace(cw, 1) // 4, 4), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            swk.sa_window_attn(cw, qs[0], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, wsw)
+        ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ew0.record(stream)
+        for _ in range(20):
+            swk.sa_window_attn(cw, qs[0], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, wsw)
+        ew1.record(stream)
+        torch.cuda.synchronize()
+        us_w = ew0.elapsed_time(ew1) * 1e3 / 20
+        fl_w = attn_flops(T, (n_s + n_l) * T, H, D)
+        windows[f"{n_s}+{n_l}"] = {"attention_avg_us": round(us_w, 1), "TFLOPs": round(fl_w / (us_w * 1e-6) / 1e12, 1)}
+        cw.close()
+    windows["3+9"] = {"attention_avg_us": round(att_avg * 1e3, 1), "TFLOPs": round(achieved, 1)}
+
     # Standalone RoPE (Q of one frame, read + write) and the KV recache.
     qrot = torch.empty_like(qs[0])
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -380,6 +402,8 @@ def main():
                      "median_launch_us": round(att_ms[len(att_ms) // 2] * 1e3, 2)},
         "append": {"avg_us": round(app_avg * 1e3, 2), "bytes": append_bytes,
                    "GBps": round(append_bytes / (app_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBPS},
+        "window_variants": {"note": "sink+local frames; one 1560-query frame, frame-causal, steady state",
+                            **windows},
         "sink_mass": {"avg_us": round(mass_us, 1),
                       "vs_attention_only": round(mass_us / (att_avg * 1e3), 3),
                       "note": "sa_window_attn_sink_mass: the attention plus each row's softmax mass on the "

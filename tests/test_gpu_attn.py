@@ -117,6 +117,26 @@ def test_cfg2_wan_layer_stream(splits, waves):
                 _check(gs, q, o, True, rows=rows, what=f"cfg2 frame {f} splits {splits} waves {waves}")
 
 
+@pytest.mark.parametrize("n_sink,n_local", [(0, 3), (0, 12), (0, 24), (3, 9)])
+def test_window_size_variants_wan_layer(n_sink, n_local):
+    """The window sizes the LongLive review compares (section "short-window attention and frame sink"
+    table: 3, 12 and 24 latent frames, and 9 local + 3 sink) at the Wan-1.3B layer shapes: streamed past
+    the first eviction, sampled rows checked while filling and in steady state."""
+    import dataclasses
+    swk = _swk()
+    w = dataclasses.replace(wl.WORKLOADS[2], name=f"window-{n_sink}-{n_local}", n_sink=n_sink, n_local=n_local,
+                            frames=n_sink + n_local + 2)
+    gs = GpuStream(w)
+    rows = sample_rows(w.tokens_per_frame, w.tokens_per_frame, n=48, seed=n_local)
+    check = {0, n_sink + n_local - 1, w.frames - 1}
+    for f in range(w.frames):
+        q, k, v = (wl.frame_qkv(w, f, tensor=t) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+        gs.append(k, v, 1, f)
+        if f in check:
+            o = gs.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
+            _check(gs, q, o, True, rows=rows, what=f"window {n_sink}+{n_local} frame {f}")
+
+
 def test_cfg2_unscaled_scores_and_custom_scale():
     """Second draw: unscaled N(0,1) Q and K (score std ~ 1) and a non-default scale (score std ~ 0.6).
 
