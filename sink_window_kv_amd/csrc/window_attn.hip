@@ -310,6 +310,21 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
     pl_b0 = blk_bytes(0);
     pl_b1 = blk_bytes(min(1, n_res - 1));
   }
+  // Lane parts of the byte offsets of a tile that lies inside one frame:
+  // key row r, chunk c -> r*D*2 + c*16; V^T row d, key chunk c -> d*T*2 + c*16.
+  uint32_t klane[KI], vlane[VI];
+#pragma unroll
+  for (int u = 0; u < KI; ++u) {
+    const int P = 64 * (wave_u * KI + u) + lane;
+    const int r = P / CPR, c = (P % CPR) ^ kswz<D>(r);
+    klane[u] = static_cast<uint32_t>(r * (D * 2) + c * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < VI; ++u) {
+    const int P = 64 * (wave_u * VI + u) + lane;
+    const int d = P / 8, c = (P % 8) ^ vswz(d);
+    vlane[u] = static_cast<uint32_t>(d * T * 2 + c * 16);
+  }
   auto plan_tile = [&](int kt) {
     TilePlan p;
     const int j0 = kt * kKTile;
@@ -329,6 +344,17 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
       koff1 = b1 - static_cast<uint32_t>(jb) * D * 2;
       voff0 = b0 - static_cast<uint32_t>(lf0) * T * 2;
       voff1 = b1 - static_cast<uint32_t>(jb) * 2;
+      // common case: the whole tile in frame lf0 and before kend_wg -- a
+      // scalar tile base plus the lane part (wave-uniform branch)
+      if (j0 + kKTile <= jb && j0 + kKTile <= kend_wg) {
+        const uint32_t kb = koff0 + static_cast<uint32_t>(j0) * (D * 2);
+        const uint32_t vb = voff0 + static_cast<uint32_t>(j0) * 2;
+#pragma unroll
+        for (int u = 0; u < KI; ++u) p.off[u] = kb + klane[u];
+#pragma unroll
+        for (int u = 0; u < VI; ++u) p.off[KI + u] = vb + vlane[u];
+        return p;
+      }
     }
 #pragma unroll
     for (int u = 0; u < KI; ++u) {
