@@ -237,7 +237,8 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
   const int tile_lo = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / a.n_splits);
   const int tile_hi = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / a.n_splits);
 
-  // ---- Q fragment: rotate in fp32, round to bf16 (B operand of S^T = K Q^T).
+  // ---- Q fragment: rotate in fp32, scale by softmax scale * log2(e), round
+  // to bf16 (B operand of S^T = K Q^T).
   mfma_bf16x8 qfrag[D / 16];
   {
     const int tok = row_ok ? row - qf * T : 0;
@@ -251,6 +252,8 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
         float x[8];
         unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
         rope_rotate8(a.rope, h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] *= a.scale_log2;  // scores come out in log2 units
         v = pack_bf16x8(x);
       }
       qfrag[s] = as_bf16x8(v);
@@ -264,6 +267,11 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = kNegInf;  // running (lazy) max of scaled scores, log2 units
   float l_run = 0.f;      // this half-wave's partial row sum
+  // S^T accumulators start at -m_use (m_use = m_run, or 0 while it is -inf),
+  // so the products come out as s - m_use and p = exp2 of them directly.
+  mfma_f32x16 mseed;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mseed[i] = 0.f;
 
   // Per-lane LDS operand addresses (bytes inside a stage); the key block,
   // channel block and stage enter as immediate offsets.
@@ -421,15 +429,11 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
     }
     mfma_f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
     for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read(st, kaddr[s] + kb * 32 * CPR * 16)),
-                                                            qfrag[s], sacc[kb], 0, 0, 0);
+                                                            qfrag[s], s == 0 ? mseed : sacc[kb], 0, 0, 0);
       if (do_fire && s % kFireStep == 0 && s / kFireStep < KI + VI) fire(np, s / kFireStep, nst);
     }
     // mask (register i of block kb holds key j0 + 32kb + 16(i/8) + 8hh + i%8)
@@ -441,7 +445,9 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + 16 * (i >> 3) + (i & 7) >= lim) sacc[kb][i] = kNegInf;
     }
-    const float mx = max_halves(tile_max(sacc)) * a.scale_log2;
+    // sacc holds s - m_use; raise the running max lazily (rare, wave-uniform)
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    const float mx = max_halves(tile_max(sacc)) + m_use;  // the tile's max of s
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -451,8 +457,16 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      // re-base this tile's scores and the seed of the next tiles
+      const float m_next = m_new == kNegInf ? 0.f : m_new;
+      const float shift = m_next - m_use;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] -= shift;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mseed[i] = -m_next;
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
     u32x4 pk[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -460,8 +474,8 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * s2 + 2 * w], a.scale_log2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * s2 + 2 * w + 1], a.scale_log2, -m_use));
+          const float p0 = __builtin_amdgcn_exp2f(sacc[kb][8 * s2 + 2 * w]);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[kb][8 * s2 + 2 * w + 1]);
           pk[kb][s2][w] = cvt_pk_bf16(p0, p1);
           l_run = dot2_ones(pk[kb][s2][w], l_run);
         }
