@@ -266,6 +266,37 @@ def test_values_one_gives_one_and_runs_are_deterministic():
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+def test_running_max_raises(waves):
+    """Scores that grow along the key sequence: keys of frame f scaled by (1 + f), so later tiles keep
+    exceeding the running max and the max is raised tile after tile.  Every row vs the oracle (score
+    std stays <= 1.75, inside the bf16 tolerance); then scores of std up to ~40, where p against
+    a stale max overflows to inf before the max is raised, with V = 1 so that O must be exactly 1."""
+    import torch
+    swk = _swk()
+    w = wl.Workload("growing-scores", 54, batch=1, n_heads=3, head_dim=128, dims=(44, 42, 42), grid=(10, 20),
+                    n_sink=2, n_local=6, chunk=1, frames=10, dtype="bf16")
+    with _env(SA_ATTN_WAVES=waves):
+        gs = GpuStream(w)
+        for f in range(w.frames):
+            k = wl.frame_qkv(w, f, tensor=wl.TENSOR_K, scale=0.35 * (1.0 + f))
+            v = wl.frame_qkv(w, f, tensor=wl.TENSOR_V, scale=1.0)
+            gs.append(k, v, 1, f)
+        q = wl.frame_qkv(w, w.frames - 1, tensor=wl.TENSOR_Q, scale=0.5)
+        for mask in (swk.SA_MASK_NONE, swk.SA_MASK_FRAME_CAUSAL):
+            o = gs.attend(q, 1, mask)
+            _check(gs, q, o, mask == swk.SA_MASK_FRAME_CAUSAL, what=f"growing scores mask {mask}")
+        gs1 = GpuStream(w, with_oracle=False)
+        ones = torch.ones((1, w.tokens_per_frame, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        for f in range(w.frames):
+            k = wl.frame_qkv(w, f, tensor=wl.TENSOR_K, scale=2.0 * (1.0 + f))
+            swk.sa_cache_append(gs1.cache, to_dev(k, "bf16"), ones, 1, f)
+        q = wl.frame_qkv(w, w.frames - 1, tensor=wl.TENSOR_Q, scale=2.0)
+        o = gs1.attend(q, 1, swk.SA_MASK_NONE)
+        assert torch.isfinite(o.float()).all()
+        assert (o.float() - 1.0).abs().max().item() <= 2.0 ** -8
+
+
 def test_attention_errors():
     import torch
     swk = _swk()
