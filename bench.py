@@ -63,9 +63,20 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read_per_launch": 4 * n, "copy_bytes_written_per_launch": 4 * n}), flush=True)
 
 
+def code_digest(src_path: str) -> str:
+    """sha256[:16] of a C++/HIP source with comments and blank lines removed, so
+    that editing a comment does not orphan counters taken on the same code."""
+    import re
+    text = open(src_path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
 def traffic_from_profile(kernel_src: str):
     """HBM bytes per attention launch from the committed counter summary, if it
-    was taken on the current kernel source (else None)."""
+    was taken on the current kernel code (else None)."""
     path = os.path.join(ROOT, "profiles", "attn_bf16_wan13b_counters.txt")
     if not os.path.exists(path):
         return None
@@ -74,8 +85,7 @@ def traffic_from_profile(kernel_src: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if vals.get("kernel_source_sha256_16") != digest:
+    if (vals.get("kernel_code_sha256_16") or "").split(" ")[0] != code_digest(kernel_src):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

@@ -24,9 +24,12 @@
 //     product needs: O^T += V^T P^T runs straight from registers.
 //   * V is stored transposed in the cache ([D][T] per slot, stream and head),
 //     so the V^T operand is a plain 16-byte LDS read.
-//   * q is rotated (RoPE) in fp32 as it is loaded, then rounded to bf16.
-//   * Online softmax in the exp2 domain with a lazily raised running max; the
-//     row sum is accumulated from the same bf16-rounded p the PV product uses.
+//   * q is rotated (RoPE) in fp32 as it is loaded, scaled by the softmax
+//     scale * log2(e), then rounded to bf16.
+//   * Online softmax in the exp2 domain with a lazily raised running max m:
+//     the S^T accumulators start at -m, so p = exp2 of the product with no
+//     per-score arithmetic; the row sum is accumulated from the same
+//     bf16-rounded p the PV product uses.
 //   * K and V^T tiles of 64 keys go global -> LDS by direct-to-LDS buffer
 //     loads into XOR-swizzled stages (no VGPR staging, conflict-free
 //     operand reads); per-tile frame bases come from the slot table, so sink
