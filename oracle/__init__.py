@@ -27,6 +27,8 @@ float64, written from the pages:
 * ``diagnostics`` -- per-head softmax mass on the sink frames and the
                    phase-coherence kernel C(Delta) (LoL paper review, "core
                    method" and "core innovation" paragraphs).
+* ``fp8``       -- e4m3 rounding of the FP8 cache (OCP 8-bit float, the
+                   format the reviewed model card's FP8 variant is read as).
 * ``brute``     -- pure-Python loop versions for tiny shapes, used to pin the
                    numpy versions.
 * ``stream``    -- composes the above into the per-frame stream the library
@@ -35,4 +37,4 @@ float64, written from the pages:
 Pins (tests/test_oracle_*.py) tie these to closed forms, invariants,
 library routines and brute force; see the test docstrings.
 """
-from . import rope, cache, attention, recache, project, brute, stream, diagnostics  # noqa: F401
+from . import rope, cache, attention, recache, project, brute, stream, diagnostics, fp8  # noqa: F401

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from oracle import attention as oattn
-from oracle import brute, cache as ocache, diagnostics as odiag, project as oproject, recache as orecache, rope as orope, stream as ostream
+from oracle import brute, cache as ocache, diagnostics as odiag, fp8 as ofp8, project as oproject, recache as orecache, rope as orope, stream as ostream
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(1234)
@@ -409,6 +409,35 @@ def test_p10_phase_coherence():
             re = sum(math.cos(x * dl) for x in w) / len(w)
             im = sum(math.sin(x * dl) for x in w) / len(w)
             assert abs(c[h, n].real - re) <= 1e-12 and abs(c[h, n].imag - im) <= 1e-12
+
+
+# ------------------------------------------------------------ P11 e4m3 rounding
+def test_p11_e4m3_codes_round_trip_and_known_values():
+    """Every finite code decodes (from the bit fields) to a value that rounds to itself; the decoded
+    values are strictly increasing from 0x00 to 0x7e; values fixed by the format definition."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    vals = ofp8.decode(codes)
+    np.testing.assert_array_equal(ofp8.round_e4m3(vals), vals)
+    pos = ofp8.decode(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)
+    assert ofp8.decode(0x38) == 1.0 and ofp8.decode(0x7E) == 448.0 and ofp8.decode(0x01) == 2.0 ** -9
+    assert ofp8.decode(0x08) == 2.0 ** -6 and ofp8.decode(0x07) == 7 * 2.0 ** -9 and ofp8.decode(0xC0) == -2.0
+    assert np.isnan(ofp8.decode(0x7F))
+
+
+def test_p11_e4m3_ties_to_even_and_clamp():
+    """Midpoints between neighbouring codes go to the code with an even mantissa; off-midpoint values go
+    to the nearer code; magnitudes beyond 448 clamp to 448."""
+    pos = ofp8.decode(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = ofp8.round_e4m3(mids)
+    even = np.where(np.arange(0x7E) % 2 == 0, pos[:-1], pos[1:])   # code parity = mantissa parity
+    np.testing.assert_array_equal(got, even)
+    np.testing.assert_array_equal(ofp8.round_e4m3(-mids), -even)
+    np.testing.assert_array_equal(ofp8.round_e4m3(mids - 1e-12 * pos[1:]), pos[:-1])
+    np.testing.assert_array_equal(ofp8.round_e4m3(mids + 1e-12 * pos[1:]), pos[1:])
+    np.testing.assert_array_equal(ofp8.round_e4m3([449.0, 1e9, -500.0]), [448.0, 448.0, -448.0])
+    np.testing.assert_allclose(ofp8.quantize([3.0, 1000.0], 2.0), [3.0, 896.0])
 
 
 # ------------------------------------------------------------ P7 closed forms
