@@ -54,7 +54,11 @@ typedef enum {
   SA_ERR_HIP = 7     /* HIP runtime or launch failure */
 } sa_status;
 
-typedef enum { SA_BF16 = 0, SA_F32 = 1 } sa_dtype;
+/* SA_FP8 is a cache element type only: keys and values stored as OCP e4m3
+ * (8 bits, max 448) with a per-tensor scale each (sa_cache_desc.k_scale,
+ * v_scale); the tensors such a cache exchanges at the boundary (k, v, q, o)
+ * are SA_BF16.  Supported with head_dim 128 by append, attention and read. */
+typedef enum { SA_BF16 = 0, SA_F32 = 1, SA_FP8 = 2 } sa_dtype;
 
 /* Attention mask inside a multi-frame query chunk.
  * SA_MASK_NONE: every query sees every resident frame.
@@ -139,6 +143,11 @@ typedef struct {
   sa_dtype dtype;
   void* k_store;            /* device */
   void* v_store;            /* device */
+  /* SA_FP8 only: stored key = e4m3(rotated key / k_scale), stored value =
+   * e4m3(value / v_scale), each clamped to +-448 first (round to nearest
+   * even).  Finite and > 0; ignored for the other element types. */
+  float k_scale;
+  float v_scale;
 } sa_cache_desc;
 
 typedef struct sa_cache sa_cache;

@@ -16,7 +16,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libsinkattn.so")
 
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_ALIGN, SA_ERR_STATE, SA_ERR_RANGE, SA_ERR_HIP = range(8)
-SA_BF16, SA_F32 = 0, 1
+SA_BF16, SA_F32, SA_FP8 = 0, 1, 2
 SA_MASK_NONE, SA_MASK_FRAME_CAUSAL = 0, 1
 SA_AXIS_T, SA_AXIS_H, SA_AXIS_W = 1, 2, 4
 SA_MAX_FRAMES = 64
@@ -44,7 +44,7 @@ class sa_cache_desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("tokens_per_frame", ctypes.c_int32), ("n_sink", ctypes.c_int32),
                 ("n_local", ctypes.c_int32), ("dtype", ctypes.c_int), ("k_store", ctypes.c_void_p),
-                ("v_store", ctypes.c_void_p)]
+                ("v_store", ctypes.c_void_p), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class sa_slot(ctypes.Structure):
@@ -197,20 +197,30 @@ def sa_rope3d_apply(rope: Rope, x, y, batch: int, n_frames: int, t0: int, stream
 
 
 class Cache:
-    """Owns an sa_cache handle plus its two device stores (torch tensors)."""
+    """Owns an sa_cache handle plus its two device stores (torch tensors).
 
-    def __init__(self, rope: Rope, batch: int, n_sink: int, n_local: int, dtype, device="cuda"):
+    dtype: torch.bfloat16, torch.float32, or torch.float8_e4m3fn for an e4m3
+    cache (bf16 k, v, q and o at the boundary; k_scale / v_scale divide the
+    stored values).
+    """
+
+    def __init__(self, rope: Rope, batch: int, n_sink: int, n_local: int, dtype, device="cuda",
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         import torch
-        code = SA_BF16 if dtype == torch.bfloat16 else SA_F32
+        if dtype == torch.float8_e4m3fn:
+            code, elem = SA_FP8, 1
+        else:
+            code, elem = (SA_BF16, 2) if dtype == torch.bfloat16 else (SA_F32, 4)
         d = sa_cache_desc()
         d.batch, d.n_heads, d.head_dim = batch, rope.n_heads, rope.head_dim
         d.tokens_per_frame, d.n_sink, d.n_local, d.dtype = rope.tokens_per_frame, n_sink, n_local, code
+        d.k_scale, d.v_scale = float(k_scale), float(v_scale)
         nbytes = lib().sa_cache_store_bytes(ctypes.byref(d))
         if nbytes == 0:
             raise SinkAttnError(SA_ERR_SHAPE, "sa_cache_store_bytes", "invalid cache descriptor")
-        elem = 2 if code == SA_BF16 else 4
-        self.k_store = torch.empty(nbytes // elem, dtype=dtype, device=device)
-        self.v_store = torch.empty(nbytes // elem, dtype=dtype, device=device)
+        store_dtype = torch.uint8 if code == SA_FP8 else dtype
+        self.k_store = torch.empty(nbytes // elem, dtype=store_dtype, device=device)
+        self.v_store = torch.empty(nbytes // elem, dtype=store_dtype, device=device)
         d.k_store, d.v_store = self.k_store.data_ptr(), self.v_store.data_ptr()
         h = _VP()
         _check(lib().sa_cache_create(ctypes.byref(d), rope.handle, ctypes.byref(h)), "sa_cache_create")

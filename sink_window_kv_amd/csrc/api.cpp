@@ -57,7 +57,7 @@ sa_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t elem_size(sa_dtype d) { return d == SA_BF16 ? 2 : 4; }
+size_t elem_size(sa_dtype d) { return d == SA_FP8 ? 1 : (d == SA_BF16 ? 2 : 4); }
 
 sa_status hip_fail(hipError_t e, const char* what) {
   return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -113,6 +113,8 @@ sa::CacheGeom geom(const sa_cache* c) {
   g.n_slots = c->desc.n_sink + c->desc.n_local;
   g.k_store = c->desc.k_store;
   g.v_store = c->desc.v_store;
+  g.k_scale = c->desc.dtype == SA_FP8 ? c->desc.k_scale : 1.f;
+  g.v_scale = c->desc.dtype == SA_FP8 ? c->desc.v_scale : 1.f;
   return g;
 }
 
@@ -311,7 +313,7 @@ sa_status sa_rope3d_apply(const sa_rope* rope, const void* x, void* y, sa_dtype 
 size_t sa_cache_store_bytes(const sa_cache_desc* d) {
   if (!d || d->batch < 1 || d->n_heads < 1 || (d->head_dim != 64 && d->head_dim != 128) ||
       d->tokens_per_frame < 8 || d->n_sink < 0 || d->n_local < 1 ||
-      d->n_sink + d->n_local > SA_MAX_FRAMES || (d->dtype != SA_BF16 && d->dtype != SA_F32))
+      d->n_sink + d->n_local > SA_MAX_FRAMES || (d->dtype != SA_BF16 && d->dtype != SA_F32 && d->dtype != SA_FP8))
     return 0;
   return static_cast<size_t>(d->n_sink + d->n_local) * d->batch * d->n_heads * d->tokens_per_frame *
          d->head_dim * elem_size(d->dtype);
@@ -320,7 +322,13 @@ size_t sa_cache_store_bytes(const sa_cache_desc* d) {
 sa_status sa_cache_create(const sa_cache_desc* d, const sa_rope* rope, sa_cache** out) {
   if (!d || !rope || !out) return fail(SA_ERR_NULL, "desc, rope and out must be non-NULL");
   if (!d->k_store || !d->v_store) return fail(SA_ERR_NULL, "k_store and v_store must be non-NULL");
-  if (d->dtype != SA_BF16 && d->dtype != SA_F32) return fail(SA_ERR_DTYPE, "dtype must be SA_BF16 or SA_F32");
+  if (d->dtype != SA_BF16 && d->dtype != SA_F32 && d->dtype != SA_FP8)
+    return fail(SA_ERR_DTYPE, "dtype must be SA_BF16, SA_F32 or SA_FP8");
+  if (d->dtype == SA_FP8) {
+    if (d->head_dim != 128) return fail(SA_ERR_SHAPE, "an SA_FP8 cache needs head_dim 128");
+    if (!(d->k_scale > 0.f) || !std::isfinite(d->k_scale) || !(d->v_scale > 0.f) || !std::isfinite(d->v_scale))
+      return fail(SA_ERR_RANGE, "k_scale and v_scale must be finite and > 0 for an SA_FP8 cache");
+  }
   if (d->batch < 1 || d->batch > 65535) return fail(SA_ERR_SHAPE, "batch must be in [1, 65535]");
   if (d->n_sink < 0 || d->n_local < 1 || d->n_sink + d->n_local > SA_MAX_FRAMES)
     return fail(SA_ERR_SHAPE, "need n_sink >= 0, n_local >= 1, n_sink + n_local <= %d", SA_MAX_FRAMES);
@@ -370,6 +378,7 @@ sa_status sa_cache_append(sa_cache* c, const void* k, const void* v, int32_t n_f
 sa_status sa_cache_recache(sa_cache* c, const void* x, const void* w_k, const void* w_v, int32_t hidden,
                            void* stream) {
   if (!c || !x || !w_k || !w_v) return fail(SA_ERR_NULL, "cache, x, w_k and w_v must be non-NULL");
+  if (c->desc.dtype == SA_FP8) return fail(SA_ERR_DTYPE, "recache into an SA_FP8 cache is not supported");
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v)) return fail(SA_ERR_ALIGN, "x and weights must be 16-byte aligned");
   const int hd = c->desc.n_heads * c->desc.head_dim;
   if (sa_status s = check_proj_sizes(0, hidden, hd, elem_size(c->desc.dtype))) return s;
@@ -388,6 +397,7 @@ sa_status sa_cache_project_append(sa_cache* c, const void* x, const void* w_q, c
                                   int32_t hidden, void* q_out, int32_t n_frames, int64_t t0, void* stream) {
   if (!c || !x || !w_k || !w_v) return fail(SA_ERR_NULL, "cache, x, w_k and w_v must be non-NULL");
   if (!w_q != !q_out) return fail(SA_ERR_NULL, "w_q and q_out must both be given or both be NULL");
+  if (c->desc.dtype == SA_FP8) return fail(SA_ERR_DTYPE, "projection into an SA_FP8 cache is not supported");
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(w_q) || !aligned16(q_out))
     return fail(SA_ERR_ALIGN, "x, weights and q_out must be 16-byte aligned");
   if (t0 < 0 || t0 > (int64_t(1) << 40)) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40]");
@@ -521,6 +531,7 @@ sa_status sa_window_attn_sink_mass(const sa_cache* c, const void* q, void* o, fl
                                    float scale, sa_mask mask, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   if (!sink_mass) return fail(SA_ERR_NULL, "sink_mass must be non-NULL");
+  if (c && c->desc.dtype == SA_FP8) return fail(SA_ERR_DTYPE, "the sink mass is not supported for an SA_FP8 cache");
   if (!aligned16(sink_mass)) return fail(SA_ERR_ALIGN, "sink_mass must be 16-byte aligned");
   if (sa_status s = check_attn(c, q, o, n_q, scale, mask, workspace, workspace_bytes)) return s;
   sa::AttnArgs a = attn_args(c, q, o, n_q, scale, mask, workspace);

@@ -10,7 +10,7 @@
 
 namespace sa {
 
-enum ElemType : int { kBF16 = 0, kF32 = 1 };
+enum ElemType : int { kBF16 = 0, kF32 = 1, kFP8 = 2 };  // kFP8: cache only (e4m3)
 
 // Device view of a RoPE handle.
 struct RopeArgs {
@@ -37,6 +37,7 @@ struct CacheGeom {
   int32_t n_slots;     // n_sink + n_local
   void* k_store;       // [n_slots][B][H][T][D]
   void* v_store;       // [n_slots][B][H][D][T]
+  float k_scale, v_scale;  // e4m3 caches: stored = value / scale
 };
 
 struct AttnArgs {

@@ -214,6 +214,88 @@ __global__ void __launch_bounds__(256) append_kv_bf16_kernel(RopeArgs rope, Cach
   }
 }
 
+// e4m3 (OCP) bytes of 8 values x * inv, clamped to +-448 (the converter
+// rounds to nearest even and does not saturate).
+__device__ __forceinline__ uint2 to_e4m3x8(const float x[8], float inv) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] * inv, -448.f), 448.f);
+  uint2 r;
+  r.x = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
+  r.x = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r.x, true);
+  r.y = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0u, false);
+  r.y = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], r.y, true);
+  return r;
+}
+
+// The same append into an e4m3 cache: bf16 k and v in, K rotated in fp32,
+// divided by k_scale, V divided by v_scale, both rounded to e4m3; 8-byte
+// stores (V^T rows are T bytes, T % 8 == 0).
+template <int D>
+__global__ void __launch_bounds__(256) append_kv_fp8_kernel(RopeArgs rope, CacheGeom g,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             FrameTable chunk) {
+  constexpr int VE = 8;                      // bf16 per 16-byte input vector
+  constexpr int DW = 64;                     // channels per workgroup
+  constexpr int VPR = DW / VE;               // vectors per token row piece
+  constexpr int NV = kVTileTok * VPR / 256;  // vectors per thread (K and V each)
+  static_assert(NV * 256 == kVTileTok * VPR, "whole tile per workgroup");
+  __shared__ uint16_t tile[kVTileTok][DW + VE];
+  constexpr int parts = D / DW;
+  const int tok0 = (blockIdx.x / parts) * kVTileTok;
+  const int d0 = (blockIdx.x % parts) * DW;
+  const int h = blockIdx.y;
+  const int j = blockIdx.z % chunk.n;
+  const int b = blockIdx.z / chunk.n;
+  const int T = g.T;
+  const int64_t src0 = ((static_cast<int64_t>(b) * chunk.n + j) * T * g.H + h) * D + d0;
+  const uint64_t src_tok_stride = static_cast<uint64_t>(g.H) * D;
+  u32x4 kv[NV], vv[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int r = e / VPR, cv = e % VPR;
+    const int tok = min(tok0 + r, T - 1);
+    const uint64_t off = static_cast<uint64_t>(tok) * src_tok_stride + cv * VE;
+    kv[u] = *reinterpret_cast<const u32x4*>(k + src0 + off);
+    vv[u] = *reinterpret_cast<const u32x4*>(v + src0 + off);
+  }
+  const int slot = chunk.store_slot[j];
+  const uint32_t blk = ((static_cast<uint32_t>(slot) * g.B + b) * g.H + h) * static_cast<uint32_t>(T) * D;
+  uint8_t* kst = static_cast<uint8_t*>(g.k_store);
+  uint8_t* vst = static_cast<uint8_t*>(g.v_store);
+  const float kinv = 1.f / g.k_scale, vinv = 1.f / g.v_scale;
+  const int64_t t = chunk.t[j];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int r = e / VPR, cv = e % VPR;
+    const int tok = tok0 + r;
+    *reinterpret_cast<u32x4*>(&tile[r][cv * VE]) = vv[u];
+    if (tok < T) {
+      float x[8];
+      unpack_bf16x8(kv[u], x);
+      rope_rotate8(rope, h, d0 / 8 + cv, t, tok / rope.grid_w, tok % rope.grid_w, x);
+      *reinterpret_cast<uint2*>(kst + blk + static_cast<uint32_t>(tok) * D + d0 + cv * VE) = to_e4m3x8(x, kinv);
+    }
+  }
+  __syncthreads();
+  constexpr int VPC = kVTileTok / VE;  // 8-token output pieces per row
+#pragma unroll
+  for (int u = 0; u < DW * VPC / 256; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int d = e / VPC, cv = e % VPC;
+    const int tok = tok0 + cv * VE;
+    if (tok < T) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < VE; ++i) x[i] = bf16_bits_to_f32(tile[cv * VE + i][d]);
+      *reinterpret_cast<uint2*>(vst + blk + static_cast<uint32_t>(d0 + d) * T + tok) = to_e4m3x8(x, vinv);
+    }
+  }
+}
+
 // Copy one stored frame out in the boundary layout [B, T, H, D].
 template <typename E>
 __global__ void __launch_bounds__(256) read_kernel(CacheGeom g, int slot, E* __restrict__ k_out,
@@ -263,7 +345,15 @@ hipError_t launch_append(const RopeArgs& rope, const CacheGeom& g, const void* k
                          int dtype, const FrameTable& chunk, hipStream_t stream) {
   const int64_t work = static_cast<int64_t>(g.B) * chunk.n * g.T * g.H * (g.D / 8);
   const dim3 vgrid((g.T + kVTileTok - 1) / kVTileTok, g.H, g.B * chunk.n);
-  if (dtype == kBF16) {
+  if (dtype == kFP8) {
+    const dim3 kvgrid(vgrid.x * (g.D / 64), vgrid.y, vgrid.z);
+    if (g.D == 128)
+      hipLaunchKernelGGL(append_kv_fp8_kernel<128>, kvgrid, dim3(256), 0, stream, rope, g,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk);
+    else
+      hipLaunchKernelGGL(append_kv_fp8_kernel<64>, kvgrid, dim3(256), 0, stream, rope, g,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk);
+  } else if (dtype == kBF16) {
     const dim3 kvgrid(vgrid.x * (g.D / 64), vgrid.y, vgrid.z);
     if (g.D == 128)
       hipLaunchKernelGGL(append_kv_bf16_kernel<128>, kvgrid, dim3(256), 0, stream, rope, g,
@@ -287,7 +377,10 @@ hipError_t launch_append(const RopeArgs& rope, const CacheGeom& g, const void* k
 hipError_t launch_read(const CacheGeom& g, int store_slot, void* k_out, void* v_out, int dtype,
                        hipStream_t stream) {
   const int64_t work = static_cast<int64_t>(g.B) * g.T * g.H * g.D;
-  if (dtype == kBF16)
+  if (dtype == kFP8)
+    hipLaunchKernelGGL(read_kernel<uint8_t>, dim3(grid_for(work)), dim3(256), 0, stream, g,
+                       store_slot, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out));
+  else if (dtype == kBF16)
     hipLaunchKernelGGL(read_kernel<uint16_t>, dim3(grid_for(work)), dim3(256), 0, stream, g,
                        store_slot, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
   else

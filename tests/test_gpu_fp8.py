@@ -1,0 +1,187 @@
+"""GPU parity of the e4m3 (FP8) cache: stored codes vs the oracle's rounding, attention vs the fp64 oracle.
+
+Two references for the attention:
+* the exact oracle on the bf16 inputs, at the FP8 tolerance below;
+* the oracle with the cache's K and V replaced by their e4m3-rounded values (oracle/fp8.py), at a
+  tighter tolerance: what remains is q and p at e4m3 precision and the bf16 output.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import fp8 as ofp8
+from swk_testutil import log, metrics, sample_rows, to_dev, to_np
+from test_gpu_attn import GpuStream, _env, _swk
+
+pytestmark = pytest.mark.gpu
+
+# e4m3 keeps 3 mantissa bits: each rounding has a relative error up to 2^-4
+# (half an ulp) and about 2^-5 RMS.  The output is a p-weighted average of V;
+# for random V its size and the error from rounding the p both shrink as
+# 1/sqrt(effective keys), so the relative error stays near the per-element
+# RMS whatever the window.  Four roundings reach the output against the
+# exact oracle (K and V in the cache, q and p in the kernel): rel-L2 bound
+# 2^-3.  Two against the oracle with e4m3 K and V (q and p): bound 2^-4.
+# Max-abs bounds for V ~ N(0, 1): 0.6 and 0.3.
+FP8_REL, FP8_ABS = 2.0 ** -3, 0.6
+FP8Q_REL, FP8Q_ABS = 2.0 ** -4, 0.3
+
+
+class Fp8Stream(GpuStream):
+    """A GpuStream over an e4m3 cache; the oracle also keeps a copy with e4m3-rounded K and V."""
+
+    def __init__(self, w, k_scale, v_scale, eps=None):
+        import torch
+        import copy
+        swk = _swk()
+        super().__init__(w, eps=eps)
+        self.cache = swk.Cache(self.rope, w.batch, w.n_sink, w.n_local, torch.float8_e4m3fn,
+                               k_scale=k_scale, v_scale=v_scale)
+        self.ks, self.vs = k_scale, v_scale
+        self.qoracle = copy.deepcopy(self.oracle)
+
+    def append(self, k, v, n, t0):
+        _swk().sa_cache_append(self.cache, to_dev(k, "bf16"), to_dev(v, "bf16"), n, t0)
+        self.oracle.append(k, v, t0)
+        self.qoracle.append(k, v, t0)
+        for f in self.qoracle.resident()[-n:]:
+            kf, vf = self.qoracle.model.k[f], self.qoracle.model.v[f]
+            self.qoracle.model.k[f] = ofp8.quantize(kf, self.ks)
+            self.qoracle.model.v[f] = ofp8.quantize(vf, self.vs)
+
+    def attend(self, q, n_q, mask, scale=0.0):
+        import torch
+        swk = _swk()
+        tq = to_dev(q, "bf16")
+        o = torch.empty_like(tq)
+        nbytes = swk.sa_window_attn_workspace(self.cache, n_q)
+        ws = torch.zeros(max(nbytes // 4, 4), dtype=torch.float32, device="cuda")
+        swk.sa_window_attn(self.cache, tq, o, n_q, scale, mask, ws)
+        torch.cuda.synchronize()
+        return o
+
+
+def _check_fp8(gs, q, o, causal, rows=None, what=""):
+    got = to_np(o)
+    if rows is not None:
+        got = got[:, rows]
+    ref = gs.oracle.attend(q, causal=causal, rows=rows)
+    qref = gs.qoracle.attend(q, causal=causal, rows=rows)
+    rel, mx = metrics(got, ref)
+    qrel, qmx = metrics(got, qref)
+    log(f"  {what}: vs exact rel_l2 {rel:.2e} max_abs {mx:.2e} | vs e4m3 K/V rel_l2 {qrel:.2e} max_abs {qmx:.2e}")
+    assert np.isfinite(got).all(), what
+    assert rel <= FP8_REL and mx <= FP8_ABS, f"{what}: vs exact rel {rel:.3e} max {mx:.3e}"
+    assert qrel <= FP8Q_REL and qmx <= FP8Q_ABS, f"{what}: vs e4m3 K/V rel {qrel:.3e} max {qmx:.3e}"
+
+
+def _read_codes(gs, idx):
+    import torch
+    w = gs.w
+    shape = (w.batch, w.tokens_per_frame, w.n_heads, w.head_dim)
+    ko = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    vo = torch.empty_like(ko)
+    _swk().sa_cache_read(gs.cache, idx, ko, vo)
+    torch.cuda.synchronize()
+    return ko.cpu().numpy(), vo.cpu().numpy()
+
+
+def _assert_valid_rounding(codes, exact, what):
+    """Stored codes equal the oracle's rounding of the exact value, except where the exact value sits
+    within fp32 rounding of a midpoint (the kernel rotates and scales in fp32): there either neighbour
+    is accepted."""
+    got = ofp8.decode(codes)
+    ref = ofp8.round_e4m3(exact)
+    diff = got != ref
+    if diff.any():
+        e = np.clip(np.abs(exact[diff]), 0, ofp8.MAX)
+        _, ex = np.frexp(e)
+        ulp = np.exp2(np.maximum(ex - 1, -6) - 3.0)
+        assert np.all(np.abs(got[diff] - exact[diff]) <= 0.5 * ulp * (1 + 2.0 ** -12) + 1e-30), what
+    frac = diff.mean()
+    log(f"  {what}: {frac:.2e} of codes at an fp32-level tie")
+    assert frac <= 1e-3, what
+
+
+SMALL = wl.Workload("fp8-small", 55, batch=2, n_heads=3, head_dim=128, dims=(44, 42, 42), grid=(6, 20),
+                    n_sink=2, n_local=4, chunk=1, frames=9, dtype="bf16", sigma=0.8)
+
+
+def test_fp8_append_codes():
+    """K = e4m3(RoPE(k) / k_scale), V = e4m3(v / v_scale), values beyond 448 * scale clamped."""
+    w = SMALL
+    gs = Fp8Stream(w, k_scale=0.25, v_scale=0.5, eps=wl.head_jitter(w))
+    for f in range(w.frames):
+        k = wl.frame_qkv(w, f, tensor=wl.TENSOR_K, scale=1.0)
+        v = wl.frame_qkv(w, f, tensor=wl.TENSOR_V, scale=1.0)
+        if f == 3:   # a few values past the clamp: 448 * 0.25 = 112, 448 * 0.5 = 224
+            k[0, :4, 0, :4] = 150.0
+            v[0, :4, 0, :4] = -300.0
+        gs.append(k, v, 1, f)
+    res = gs.oracle.resident()
+    for idx, f in enumerate(res):
+        kc, vc = _read_codes(gs, idx)
+        kref, vref = gs.oracle.frame_kv(f)
+        _assert_valid_rounding(kc, kref / gs.ks, f"K codes frame {f}")
+        _assert_valid_rounding(vc, vref / gs.vs, f"V codes frame {f}")
+
+
+@pytest.mark.parametrize("chunks,mask", [([1] * 9, 1), ([1] * 9, 0), ([3, 3, 3], 1)])
+def test_fp8_attention_small(chunks, mask):
+    """Both masks and 3-frame frame-causal chunks over 2 streams; every row; tiles end inside every frame
+    (120 tokens a frame: one full and one partial 64-key tile)."""
+    swk = _swk()
+    w = SMALL
+    gs = Fp8Stream(w, k_scale=1.0 / 64, v_scale=1.0 / 64, eps=wl.head_jitter(w))
+    f0 = 0
+    for c in chunks:
+        q, k, v = (wl.chunk_qkv(w, f0, c, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+        gs.append(k, v, c, f0)
+        o = gs.attend(q, c, mask)
+        _check_fp8(gs, q, o, mask == swk.SA_MASK_FRAME_CAUSAL, what=f"chunk at {f0} mask {mask}")
+        f0 += c
+
+
+@pytest.mark.parametrize("splits", [None, "1", "5"])
+def test_fp8_attention_wan_layer(splits):
+    """Wan-1.3B layer in an e4m3 cache: 3 sink + 9 local frames of 1560 tokens (24 full tiles and one of
+    24 keys per frame), sampled rows while filling and in steady state; unscaled N(0,1) q and k."""
+    swk = _swk()
+    w = wl.WORKLOADS[2]
+    rows = sample_rows(w.tokens_per_frame, w.tokens_per_frame, n=64, seed=11)
+    with _env(SA_ATTN_SPLITS=splits):
+        gs = Fp8Stream(w, k_scale=1.0 / 64, v_scale=1.0 / 64)
+        for f in range(14):
+            q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+            gs.append(k, v, 1, f)
+            if f in (0, 2, 11, 13):
+                o = gs.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
+                _check_fp8(gs, q, o, True, rows=rows, what=f"wan fp8 frame {f} splits {splits}")
+
+
+def test_fp8_cache_errors():
+    import torch
+    swk = _swk()
+    w = SMALL
+    rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid)
+    with pytest.raises(swk.SinkAttnError) as e:
+        swk.Cache(rope, 1, 1, 2, torch.float8_e4m3fn, k_scale=0.0)
+    assert e.value.status == swk.SA_ERR_RANGE
+    r64 = swk.Rope(2, 64, (22, 22, 20), (4, 8))
+    with pytest.raises(swk.SinkAttnError) as e:
+        swk.Cache(r64, 1, 1, 2, torch.float8_e4m3fn)
+    assert e.value.status == swk.SA_ERR_SHAPE
+    gs = Fp8Stream(w, 1.0, 1.0)
+    k = wl.frame_qkv(w, 0, tensor=wl.TENSOR_K)
+    gs.append(k, k, 1, 0)
+    tq = to_dev(k, "bf16")
+    o = torch.empty_like(tq)
+    mass = torch.empty((w.batch, w.tokens_per_frame, w.n_heads), dtype=torch.float32, device="cuda")
+    with pytest.raises(swk.SinkAttnError) as e:
+        swk.sa_window_attn_sink_mass(gs.cache, tq, o, mass, 1)
+    assert e.value.status == swk.SA_ERR_DTYPE
+    x = torch.zeros((w.batch, w.tokens_per_frame, 64), dtype=torch.bfloat16, device="cuda")
+    wt = torch.zeros((w.n_heads * w.head_dim, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(swk.SinkAttnError) as e:
+        swk.sa_cache_recache(gs.cache, x, wt, wt, 64)
+    assert e.value.status == swk.SA_ERR_DTYPE
