@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (vendor figure)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 (e4m3) MFMA (vendor figure)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 N_LAYERS = 8
 
@@ -381,7 +382,59 @@ def main():
           f"({flops5 / (a5_avg * 1e-3) / 1e12:.0f} TFLOP/s), append {ap5_avg * 1e3:.1f} us",
           file=sys.stderr, flush=True)
     c5.close()
+
+    # FP8 (e4m3) cache: the same frame step (append + attention, 8 layer
+    # caches cycled) and the B = 4 chunk, with the cache in e4m3.
+    f8 = torch.float8_e4m3fn
+    c8s = [swk.Cache(rope, 1, w.n_sink, w.n_local, f8, device=dev, k_scale=1.0 / 256, v_scale=1.0 / 256)
+           for _ in range(N_LAYERS)]
+    t8 = [0] * N_LAYERS
+    for li, c in enumerate(c8s):
+        for f in range(n_win):
+            swk.sa_cache_append(c, ks[(f + li) % pool], vs[(f + li) % pool], 1, t8[li])
+            t8[li] += 1
+    ws8 = torch.zeros(max(max(swk.sa_window_attn_workspace(c, 1) for c in c8s) // 4, 4), dtype=torch.float32,
+                      device=dev)
+    n8, skip8 = 120, 20
+    ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n8)]
+    for i in range(n8):
+        li = i % N_LAYERS
+        fi = (t8[li] + li) % pool
+        ev8[i][0].record(stream)
+        swk.sa_cache_append(c8s[li], ks[fi], vs[fi], 1, t8[li])
+        ev8[i][1].record(stream)
+        swk.sa_window_attn(c8s[li], qs[fi], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws8)
+        ev8[i][2].record(stream)
+        t8[li] += 1
+    torch.cuda.synchronize()
+    a8 = sum(e[1].elapsed_time(e[2]) for e in ev8[skip8:]) / (n8 - skip8)
+    p8 = sum(e[0].elapsed_time(e[1]) for e in ev8[skip8:]) / (n8 - skip8)
+    for c in c8s:
+        c.close()
+    c58 = swk.Cache(rope5, w5.batch, w5.n_sink, w5.n_local, f8, device=dev, k_scale=1.0 / 256, v_scale=1.0 / 256)
+    t58 = 0
+    for ci in range(4):
+        swk.sa_cache_append(c58, chunks5[ci][1], chunks5[ci][2], w5.chunk, t58)
+        t58 += w5.chunk
+    ws58 = torch.zeros(max(swk.sa_window_attn_workspace(c58, w5.chunk) // 4, 4), dtype=torch.float32, device=dev)
+    a58_ms = []
+    for it in range(13):
+        q5, k5, v5 = chunks5[it % 4]
+        swk.sa_cache_append(c58, k5, v5, w5.chunk, t58)
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record(stream)
+        swk.sa_window_attn(c58, q5, o5, w5.chunk, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws58)
+        eb.record(stream)
+        t58 += w5.chunk
+        torch.cuda.synchronize()
+        if it >= 3:
+            a58_ms.append(ea.elapsed_time(eb))
+    a58 = sum(a58_ms) / len(a58_ms)
+    c58.close()
     rope5.close()
+    print(f"[bench] fp8 cache: attention {a8 * 1e3:.1f} us ({flops / (a8 * 1e-3) / 1e12:.0f} TFLOP/s), "
+          f"append {p8 * 1e3:.1f} us; B=4 chunks {a58 * 1e3:.1f} us ({flops5 / (a58 * 1e-3) / 1e12:.0f} TFLOP/s)",
+          file=sys.stderr, flush=True)
 
     traffic = traffic_from_profile(os.path.join(ROOT, "sink_window_kv_amd", "csrc", "window_attn.hip"))
     out = {
@@ -440,6 +493,15 @@ def main():
                        "pct_bf16_peak": round(100.0 * flops5 / (a5_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                        "append_avg_us": round(ap5_avg * 1e3, 1),
                        "latent_frames_per_s_per_layer": round(w5.batch * w5.chunk / ((a5_avg + ap5_avg) * 1e-3), 1)},
+        "fp8_cache": {"workload": "the same two workloads with the KV cache in OCP e4m3 (per-tensor scales); "
+                                  "q and p rounded to e4m3 in the kernel; bf16 in and out",
+                      "attention_avg_us": round(a8 * 1e3, 1),
+                      "TFLOPs": round(flops / (a8 * 1e-3) / 1e12, 1),
+                      "pct_fp8_peak": round(100.0 * flops / (a8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+                      "append_avg_us": round(p8 * 1e3, 1),
+                      "latent_frames_per_s_per_layer": round(1e3 / (a8 + p8), 1),
+                      "b4_chunk_attention_avg_us": round(a58 * 1e3, 1),
+                      "b4_chunk_TFLOPs": round(flops5 / (a58 * 1e-3) / 1e12, 1)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
