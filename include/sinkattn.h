@@ -185,8 +185,10 @@ sa_status sa_cache_append(sa_cache* cache, const void* k, const void* v, int32_t
  *                                     logical order (sinks, then local oldest -> newest)
  *   w_k, w_v [H*D, hidden]            projection weights in the nn.Linear
  *                                     [out, in] layout: row h*D+d makes channel d of head h
- * All of the cache's dtype.  hidden must be a multiple of 32.  SA_ERR_STATE on
- * an empty cache. */
+ * All of the cache's dtype (bf16 for an SA_FP8 cache, whose keys and values
+ * are then the bf16-rounded results divided by k_scale / v_scale and rounded
+ * to e4m3).  hidden must be a multiple of 32.  SA_ERR_STATE on an empty
+ * cache. */
 sa_status sa_cache_recache(sa_cache* cache, const void* x, const void* w_k, const void* w_v,
                            int32_t hidden, void* stream);
 
@@ -204,8 +206,9 @@ sa_status sa_cache_recache(sa_cache* cache, const void* x, const void* w_k, cons
  *                                     channel d of head h
  *   q_out  [B, n_frames*T_f, H, D]    may be NULL together with w_q (then
  *                                     only the cache is written)
- * All of the cache's dtype.  hidden must be a multiple of 32.  The same
- * chunk and time rules as sa_cache_append apply (SA_ERR_RANGE/SHAPE). */
+ * All of the cache's dtype (bf16 for an SA_FP8 cache, as for the recache).
+ * hidden must be a multiple of 32.  The same chunk and time rules as
+ * sa_cache_append apply (SA_ERR_RANGE/SHAPE). */
 sa_status sa_cache_project_append(sa_cache* cache, const void* x, const void* w_q, const void* w_k,
                                   const void* w_v, int32_t hidden, void* q_out, int32_t n_frames,
                                   int64_t t0, void* stream);

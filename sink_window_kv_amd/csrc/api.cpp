@@ -166,6 +166,11 @@ sa_status check_proj_sizes(int64_t n_tok, int32_t hidden, int32_t width, size_t 
   return SA_OK;
 }
 
+// The projection GEMM's element type for this cache: an e4m3 cache takes
+// bf16 x, weights and q.
+int proj_dtype(const sa_cache* c) { return c->desc.dtype == SA_FP8 ? sa::kBF16 : static_cast<int>(c->desc.dtype); }
+size_t proj_elem_size(const sa_cache* c) { return c->desc.dtype == SA_F32 ? 4 : 2; }
+
 // Projection segments into this cache: [q rows,] rotated keys, values.
 sa::ProjArgs cache_proj_args(const sa_cache* c, const void* x, const void* w_q, void* q_out, const void* w_k,
                              const void* w_v, int32_t hidden) {
@@ -181,6 +186,7 @@ sa::ProjArgs cache_proj_args(const sa_cache* c, const void* x, const void* w_q, 
   for (int i = n; i < 3; ++i) a.seg[i] = a.seg[n - 1];
   a.has_key = 1;
   a.has_value = 1;
+  a.cache_fp8 = c->desc.dtype == SA_FP8 ? 1 : 0;
   a.g = geom(c);
   a.rope = rope_args(c->rope);
   return a;
@@ -378,17 +384,16 @@ sa_status sa_cache_append(sa_cache* c, const void* k, const void* v, int32_t n_f
 sa_status sa_cache_recache(sa_cache* c, const void* x, const void* w_k, const void* w_v, int32_t hidden,
                            void* stream) {
   if (!c || !x || !w_k || !w_v) return fail(SA_ERR_NULL, "cache, x, w_k and w_v must be non-NULL");
-  if (c->desc.dtype == SA_FP8) return fail(SA_ERR_DTYPE, "recache into an SA_FP8 cache is not supported");
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v)) return fail(SA_ERR_ALIGN, "x and weights must be 16-byte aligned");
   const int hd = c->desc.n_heads * c->desc.head_dim;
-  if (sa_status s = check_proj_sizes(0, hidden, hd, elem_size(c->desc.dtype))) return s;
+  if (sa_status s = check_proj_sizes(0, hidden, hd, proj_elem_size(c))) return s;
   if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "recache on an empty cache");
   const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * c->plan.resident().size() * c->desc.tokens_per_frame;
-  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, elem_size(c->desc.dtype))) return s;
+  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, proj_elem_size(c))) return s;
   sa::ProjArgs a = cache_proj_args(c, x, nullptr, nullptr, w_k, w_v, hidden);
   a.n_tok = n_tok;
   a.frames = resident_table(c);
-  const hipError_t e = sa::launch_proj(a, c->desc.dtype, device_cus(), static_cast<hipStream_t>(stream));
+  const hipError_t e = sa::launch_proj(a, proj_dtype(c), device_cus(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "recache launch");
   return ok();
 }
@@ -397,18 +402,17 @@ sa_status sa_cache_project_append(sa_cache* c, const void* x, const void* w_q, c
                                   int32_t hidden, void* q_out, int32_t n_frames, int64_t t0, void* stream) {
   if (!c || !x || !w_k || !w_v) return fail(SA_ERR_NULL, "cache, x, w_k and w_v must be non-NULL");
   if (!w_q != !q_out) return fail(SA_ERR_NULL, "w_q and q_out must both be given or both be NULL");
-  if (c->desc.dtype == SA_FP8) return fail(SA_ERR_DTYPE, "projection into an SA_FP8 cache is not supported");
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(w_q) || !aligned16(q_out))
     return fail(SA_ERR_ALIGN, "x, weights and q_out must be 16-byte aligned");
   if (t0 < 0 || t0 > (int64_t(1) << 40)) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40]");
   if (sa_status s = check_append_chunk(c, n_frames, t0)) return s;
   const int hd = c->desc.n_heads * c->desc.head_dim;
   const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * n_frames * c->desc.tokens_per_frame;
-  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, elem_size(c->desc.dtype))) return s;
+  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, proj_elem_size(c))) return s;
   sa::ProjArgs a = cache_proj_args(c, x, w_q, q_out, w_k, w_v, hidden);
   a.n_tok = n_tok;
   a.frames = chunk_table(c, n_frames, t0);
-  const hipError_t e = sa::launch_proj(a, c->desc.dtype, device_cus(), static_cast<hipStream_t>(stream));
+  const hipError_t e = sa::launch_proj(a, proj_dtype(c), device_cus(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   c->plan.commit_append(n_frames, t0);
   return ok();

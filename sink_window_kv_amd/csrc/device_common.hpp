@@ -45,6 +45,20 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float in[8]) {
   return v;
 }
 
+// e4m3 (OCP) bytes of 8 values x * inv, clamped to +-448 first (the
+// converter rounds to nearest even and does not saturate).
+__device__ __forceinline__ uint2 to_e4m3x8(const float x[8], float inv) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] * inv, -448.f), 448.f);
+  uint2 r;
+  r.x = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
+  r.x = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r.x, true);
+  r.y = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0u, false);
+  r.y = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], r.y, true);
+  return r;
+}
+
 // Position of channel pair p for a token at (t, row, col).
 __device__ __forceinline__ double rope_pair_pos(const RopeArgs& r, int p, int64_t t, int row,
                                                 int col) {

@@ -83,6 +83,7 @@ struct ProjArgs {
   int32_t n_seg;      // 1..3; unused entries repeat a valid weight pointer
   ProjSeg seg[3];
   int32_t has_key, has_value;  // some segment is kOutCacheK / kOutCacheV
+  int32_t cache_fp8;           // cache outputs go to an e4m3 cache (bf16-rounded results, scaled)
   // Cache outputs only: token n is token tok of frame j of stream b, with
   // n = (b * frames.n + j) * T + tok.
   CacheGeom g;

@@ -13,6 +13,8 @@
 //     scattered to the key store [slot][b][h][tok][d];
 //   * value segment: scattered to the transposed value store
 //     [slot][b][h][d][tok].
+// An e4m3 cache receives the bf16-rounded results divided by its scales and
+// rounded to e4m3 (8-byte pieces).
 // Three entry points use it:
 //   * KV recache at a prompt switch (LongLive paper review, section 3 "KV
 //     Recache"): segments (W_k -> key cache, W_v -> value cache) over every
@@ -302,7 +304,14 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
       token_coords(tkn, per_stream, g.T, &b, &lf, &tok);
       const int64_t slot = a.frames.store_slot[lf];
       const int head = fs / g.D, d = fs - head * g.D;
-      *reinterpret_cast<u32x4*>(kst + (((slot * g.B + b) * g.H + head) * g.T + tok) * g.D + d) = piece;
+      const int64_t idx = (((slot * g.B + b) * g.H + head) * g.T + tok) * g.D + d;
+      if (a.cache_fp8) {
+        float x[8];
+        unpack_bf16x8(piece, x);
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(g.k_store) + idx) = to_e4m3x8(x, 1.f / g.k_scale);
+      } else {
+        *reinterpret_cast<u32x4*>(kst + idx) = piece;
+      }
     }
   }
   if (!a.has_value) return;
@@ -323,8 +332,15 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
     uint16_t vals[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) vals[r] = sm.out.o[tl + r][fl];
-    *reinterpret_cast<u32x4*>(vst + (((slot * g.B + b) * g.H + head) * g.D + d) * g.T + tok) =
-        *reinterpret_cast<const u32x4*>(vals);
+    const int64_t idx = (((slot * g.B + b) * g.H + head) * g.D + d) * g.T + tok;
+    if (a.cache_fp8) {
+      float x[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) x[r] = bf16_bits_to_f32(vals[r]);
+      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(g.v_store) + idx) = to_e4m3x8(x, 1.f / g.v_scale);
+    } else {
+      *reinterpret_cast<u32x4*>(vst + idx) = *reinterpret_cast<const u32x4*>(vals);
+    }
   }
 }
 

@@ -214,20 +214,6 @@ __global__ void __launch_bounds__(256) append_kv_bf16_kernel(RopeArgs rope, Cach
   }
 }
 
-// e4m3 (OCP) bytes of 8 values x * inv, clamped to +-448 (the converter
-// rounds to nearest even and does not saturate).
-__device__ __forceinline__ uint2 to_e4m3x8(const float x[8], float inv) {
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(x[i] * inv, -448.f), 448.f);
-  uint2 r;
-  r.x = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
-  r.x = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r.x, true);
-  r.y = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0u, false);
-  r.y = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], r.y, true);
-  return r;
-}
-
 // The same append into an e4m3 cache: bf16 k and v in, K rotated in fp32,
 // divided by k_scale, V divided by v_scale, both rounded to e4m3; 8-byte
 // stores (V^T rows are T bytes, T % 8 == 0).

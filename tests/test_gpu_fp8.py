@@ -159,6 +159,69 @@ def test_fp8_attention_wan_layer(splits):
                 _check_fp8(gs, q, o, True, rows=rows, what=f"wan fp8 frame {f} splits {splits}")
 
 
+def _assert_close_rounding(codes, exact, what):
+    """Codes written by the projection GEMM: its results are rounded to bf16 before e4m3, so each
+    decoded value is within half an e4m3 ulp plus half a bf16 ulp of the exact value (double rounding)."""
+    got = ofp8.decode(codes)
+    a = np.clip(np.abs(exact), 0, ofp8.MAX)
+    _, ex = np.frexp(a)
+    ulp8 = np.exp2(np.maximum(ex - 1, -6) - 3.0)
+    bound = 0.5 * ulp8 + np.abs(exact) * 2.0 ** -8 + 1e-30
+    assert np.all(np.abs(got - np.clip(exact, -ofp8.MAX, ofp8.MAX)) <= bound * (1 + 1e-6)), what
+
+
+def test_fp8_project_append_and_recache():
+    """q/k/v projections appended into an e4m3 cache, then a recache with new weights: the stored codes
+    against the exact projections, and the attention on the projected queries."""
+    import torch
+    from oracle import project as oproject
+    from test_gpu_project import _weights_dev
+    swk = _swk()
+    w = wl.Workload("fp8-proj", 56, batch=2, n_heads=2, head_dim=128, dims=(44, 42, 42), grid=(6, 20),
+                    n_sink=1, n_local=3, chunk=1, frames=6, dtype="bf16", sigma=0.8, hidden=192)
+    ks, vs = 1.0 / 32, 1.0 / 32
+    gs = Fp8Stream(w, ks, vs, eps=wl.head_jitter(w))
+    wq, wk, wv = wl.projection_weights(w)
+    dq, dk, dv = _weights_dev((wq, wk, wv), "bf16")
+    T = w.tokens_per_frame
+    for f in range(w.frames):
+        x = wl.frame_hidden(w, f, 1)
+        q_out = torch.empty((w.batch, T, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        swk.sa_cache_project_append(gs.cache, to_dev(x, "bf16"), dq, dk, dv, w.hidden, q_out, 1, f)
+        torch.cuda.synchronize()
+        q_ref, _ = oproject.project_append(gs.oracle, x, wq, wk, wv, w.n_heads, f)
+        oproject.project_append(gs.qoracle, x, wq, wk, wv, w.n_heads, f)
+        f_new = gs.qoracle.resident()[-1]
+        gs.qoracle.model.k[f_new] = ofp8.quantize(gs.qoracle.model.k[f_new], ks)
+        gs.qoracle.model.v[f_new] = ofp8.quantize(gs.qoracle.model.v[f_new], vs)
+        res = gs.oracle.resident()
+        kc, vc = _read_codes(gs, len(res) - 1)
+        kref, vref = gs.oracle.frame_kv(res[-1])
+        _assert_close_rounding(kc, kref / ks, f"projected K codes frame {f}")
+        _assert_close_rounding(vc, vref / vs, f"projected V codes frame {f}")
+        o = torch.empty_like(q_out)
+        nbytes = swk.sa_window_attn_workspace(gs.cache, 1)
+        ws = torch.zeros(max(nbytes // 4, 4), dtype=torch.float32, device="cuda")
+        swk.sa_window_attn(gs.cache, q_out, o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+        torch.cuda.synchronize()
+        got = to_np(o)
+        rel, mx = metrics(got, gs.oracle.attend(q_ref, causal=True))
+        log(f"  projected fp8 frame {f}: attention vs exact rel_l2 {rel:.2e} max_abs {mx:.2e}")
+        assert rel <= FP8_REL and mx <= FP8_ABS
+    # recache with fresh weights
+    res = gs.oracle.resident()
+    x, wk2, wv2 = wl.recache_inputs(w, n_frames=len(res))
+    swk.sa_cache_recache(gs.cache, to_dev(x, "bf16"), to_dev(np.ascontiguousarray(wk2.T), "bf16"),
+                         to_dev(np.ascontiguousarray(wv2.T), "bf16"), w.hidden)
+    torch.cuda.synchronize()
+    gs.oracle.recache(x, wk2, wv2)
+    for i, f in enumerate(res):
+        kc, vc = _read_codes(gs, i)
+        kref, vref = gs.oracle.frame_kv(f)
+        _assert_close_rounding(kc, kref / ks, f"recached K codes frame {f}")
+        _assert_close_rounding(vc, vref / vs, f"recached V codes frame {f}")
+
+
 def test_fp8_cache_errors():
     import torch
     swk = _swk()
@@ -179,9 +242,4 @@ def test_fp8_cache_errors():
     mass = torch.empty((w.batch, w.tokens_per_frame, w.n_heads), dtype=torch.float32, device="cuda")
     with pytest.raises(swk.SinkAttnError) as e:
         swk.sa_window_attn_sink_mass(gs.cache, tq, o, mass, 1)
-    assert e.value.status == swk.SA_ERR_DTYPE
-    x = torch.zeros((w.batch, w.tokens_per_frame, 64), dtype=torch.bfloat16, device="cuda")
-    wt = torch.zeros((w.n_heads * w.head_dim, 64), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(swk.SinkAttnError) as e:
-        swk.sa_cache_recache(gs.cache, x, wt, wt, 64)
     assert e.value.status == swk.SA_ERR_DTYPE
