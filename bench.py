@@ -64,18 +64,24 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read_per_launch": 4 * n, "copy_bytes_written_per_launch": 4 * n}), flush=True)
 
 
-def code_digest(src_path: str) -> str:
-    """sha256[:16] of a C++/HIP source with comments and blank lines removed, so
-    that editing a comment does not orphan counters taken on the same code."""
+ATTN_BF16_SOURCES = [os.path.join(ROOT, "sink_window_kv_amd", "csrc", f)
+                     for f in ("window_attn.hip", "attn_common.hpp", "device_common.hpp", "internal.hpp")]
+
+
+def code_digest(src_paths) -> str:
+    """sha256[:16] of C++/HIP sources (concatenated) with comments and blank lines
+    removed, so that editing a comment does not orphan counters taken on the same code."""
     import re
-    text = open(src_path).read()
+    if isinstance(src_paths, str):
+        src_paths = [src_paths]
+    text = "\n".join(open(p).read() for p in src_paths)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     code = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str):
+def traffic_from_profile(kernel_srcs):
     """HBM bytes per attention launch from the committed counter summary, if it
     was taken on the current kernel code (else None)."""
     path = os.path.join(ROOT, "profiles", "attn_bf16_wan13b_counters.txt")
@@ -86,7 +92,7 @@ def traffic_from_profile(kernel_src: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if (vals.get("kernel_code_sha256_16") or "").split(" ")[0] != code_digest(kernel_src):
+    if (vals.get("kernel_code_sha256_16") or "").split(" ")[0] != code_digest(kernel_srcs):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -436,7 +442,7 @@ def main():
           f"append {p8 * 1e3:.1f} us; B=4 chunks {a58 * 1e3:.1f} us ({flops5 / (a58 * 1e-3) / 1e12:.0f} TFLOP/s)",
           file=sys.stderr, flush=True)
 
-    traffic = traffic_from_profile(os.path.join(ROOT, "sink_window_kv_amd", "csrc", "window_attn.hip"))
+    traffic = traffic_from_profile(ATTN_BF16_SOURCES)
     out = {
         "metric": "sink+window attn TFLOP/s & latent frames/s/layer on 1 MI355X; % bf16 MFMA peak",
         "value": round(value, 2),

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ["api.cpp", "rope_append.hip", "window_attn.hip", "proj_gemm.hip"]
+SOURCES = ["api.cpp", "rope_append.hip", "window_attn.hip", "window_attn_fp8.hip", "proj_gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,7 +43,7 @@ def _run(cmd):
 # Per-source extra flags.  The attention kernel never sees a NaN (masked
 # scores are -inf, every finite input stays finite), so NaN-aware max/min
 # canonicalisation is dropped there.
-EXTRA = {"window_attn.hip": ["-fno-honor-nans"]}
+EXTRA = {"window_attn.hip": ["-fno-honor-nans"], "window_attn_fp8.hip": ["-fno-honor-nans"]}
 
 
 def build(jobs: int = 4, verbose: bool = False) -> str:

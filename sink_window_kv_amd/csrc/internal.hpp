@@ -105,6 +105,8 @@ int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus);
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus);
 size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits);
 hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream);
+// The e4m3 attention kernel alone (head_dim 128); launch_window_attn adds the split merge.
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream);
 
 // Tile shape the bf16 projection kernel takes for n_tok x F outputs:
 // 0 = 256 x 128, 1 = 128 x 128, 2 = 128 x 64 (features x tokens).
