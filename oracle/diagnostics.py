@@ -42,7 +42,8 @@ def sink_mass(stream, q: np.ndarray, causal: bool, scale: float | None = None, h
     res = stream.resident()
     qframes = res[-n_q:]
     t_list = [stream.model.t[f] for f in qframes]
-    q_rot = _rope.rope3d(q, 0, T, stream.bases, stream.dims, stream.grid_w, t_list=t_list)
+    q_rot = _rope.rope3d(q, 0, T, stream.bases, stream.dims, stream.grid_w, t_list=t_list,
+                         t_scale=stream.t_scale)
     B, Lq, H, D = q_rot.shape
     scale = 1.0 / np.sqrt(D) if scale is None else scale
     heads = list(range(H)) if heads is None else list(heads)
@@ -60,10 +61,14 @@ def sink_mass(stream, q: np.ndarray, causal: bool, scale: float | None = None, h
     return out
 
 
-def phase_coherence(bases: np.ndarray, dims, deltas) -> np.ndarray:
-    """C_h(Delta) for every head h (rows) and offset Delta (columns), complex128 [H, n]."""
+def phase_coherence(bases: np.ndarray, dims, deltas, t_scale: float = 1.0) -> np.ndarray:
+    """C_h(Delta) for every head h (rows) and offset Delta (columns), complex128 [H, n].
+
+    Under position interpolation a frame offset Delta is a time-position offset
+    Delta * t_scale.
+    """
     bases = np.asarray(bases, dtype=np.float64)
-    deltas = np.asarray(deltas, dtype=np.float64)
+    deltas = np.asarray(deltas, dtype=np.float64) * float(t_scale)
     out = np.empty((bases.shape[0], deltas.size), dtype=np.complex128)
     for h in range(bases.shape[0]):
         w = _rope.axis_frequencies(bases[h, 0], dims[0])       # time axis

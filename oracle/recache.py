@@ -32,7 +32,7 @@ def project(x: np.ndarray, w: np.ndarray, n_heads: int) -> np.ndarray:
 
 
 def recache(x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray, n_heads: int,
-            t_list, tokens_per_frame: int, bases: np.ndarray, dims, grid_w: int):
+            t_list, tokens_per_frame: int, bases: np.ndarray, dims, grid_w: int, t_scale: float = 1.0):
     """Recompute the cache of the resident frames given in logical order.
 
     x: [B, n*T_f, C]; returns (k_frames, v_frames), lists of [B, T_f, H, D],
@@ -43,6 +43,6 @@ def recache(x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray, n_heads: int,
     k_frames, v_frames = [], []
     for j, t in enumerate(t_list):
         sl = slice(j * tokens_per_frame, (j + 1) * tokens_per_frame)
-        k_frames.append(_rope.rope3d_frame(k[:, sl], t, bases, dims, grid_w))
+        k_frames.append(_rope.rope3d_frame(k[:, sl], t, bases, dims, grid_w, t_scale))
         v_frames.append(v[:, sl])
     return k_frames, v_frames

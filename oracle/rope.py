@@ -24,6 +24,11 @@ Readings taken where the pages are silent or garbled:
   others.  One eps per head, shared by Q and K, all frames and all streams.
 * Positions: t is the latent frame's time index; token i of a frame sits at
   row i // grid_w, column i % grid_w.
+* Position interpolation (PI), the baseline the LoL review's results compare
+  against (it compresses positions, which ends the collapse but also most of
+  the motion): the time position of a frame becomes t * t_scale with a
+  compression factor t_scale (1 = none); the grid positions are unchanged.
+  The review gives no factor, so it is a parameter.
 """
 from __future__ import annotations
 
@@ -57,10 +62,13 @@ def head_frequencies(bases_h: np.ndarray, dims) -> np.ndarray:
     return np.concatenate([axis_frequencies(bases_h[a], dims[a]) for a in range(3)])
 
 
-def pair_positions(t: int, token: np.ndarray, grid_w: int, dims) -> np.ndarray:
-    """Position of every channel pair for the given tokens: [n_tokens, D/2] float64."""
+def pair_positions(t: int, token: np.ndarray, grid_w: int, dims, t_scale: float = 1.0) -> np.ndarray:
+    """Position of every channel pair for the given tokens: [n_tokens, D/2] float64.
+
+    The time axis sits at t * t_scale (position interpolation; 1 = none).
+    """
     token = np.asarray(token, dtype=np.int64)
-    pos_axes = [np.full(token.shape, float(t)), (token // grid_w).astype(np.float64),
+    pos_axes = [np.full(token.shape, float(t) * float(t_scale)), (token // grid_w).astype(np.float64),
                 (token % grid_w).astype(np.float64)]
     cols = [np.repeat(pos_axes[a][:, None], dims[a] // 2, axis=1) for a in range(3)]
     return np.concatenate(cols, axis=1)
@@ -82,15 +90,15 @@ def rotate_pairs(x: np.ndarray, phi: np.ndarray) -> np.ndarray:
     return out
 
 
-def rope3d_frame(x: np.ndarray, t: int, bases: np.ndarray, dims, grid_w: int) -> np.ndarray:
-    """Rotate one latent frame x [B, T_f, H, D] at time t; bases [H, 3].
+def rope3d_frame(x: np.ndarray, t: int, bases: np.ndarray, dims, grid_w: int, t_scale: float = 1.0) -> np.ndarray:
+    """Rotate one latent frame x [B, T_f, H, D] at time t (position t * t_scale); bases [H, 3].
 
     LoL review, method steps (5)-(7): each head uses its own frequencies.
     """
     x = np.asarray(x, dtype=np.float64)
     B, T, H, D = x.shape
     assert sum(dims) == D and all(d % 2 == 0 for d in dims)
-    pos = pair_positions(t, np.arange(T), grid_w, dims)          # [T, D/2]
+    pos = pair_positions(t, np.arange(T), grid_w, dims, t_scale)  # [T, D/2]
     out = np.empty_like(x)
     for h in range(H):
         w = head_frequencies(bases[h], dims)                       # [D/2]
@@ -99,7 +107,7 @@ def rope3d_frame(x: np.ndarray, t: int, bases: np.ndarray, dims, grid_w: int) ->
 
 
 def rope3d(x: np.ndarray, t0: int, tokens_per_frame: int, bases: np.ndarray, dims,
-           grid_w: int, t_list=None) -> np.ndarray:
+           grid_w: int, t_list=None, t_scale: float = 1.0) -> np.ndarray:
     """Rotate x [B, n*T_f, H, D]; frame j of the token axis has time t0 + j (or t_list[j])."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[1] // tokens_per_frame
@@ -107,5 +115,5 @@ def rope3d(x: np.ndarray, t0: int, tokens_per_frame: int, bases: np.ndarray, dim
     for j in range(n):
         t = (t0 + j) if t_list is None else t_list[j]
         sl = slice(j * tokens_per_frame, (j + 1) * tokens_per_frame)
-        out[:, sl] = rope3d_frame(x[:, sl], t, bases, dims, grid_w)
+        out[:, sl] = rope3d_frame(x[:, sl], t, bases, dims, grid_w, t_scale)
     return out

@@ -440,6 +440,68 @@ def test_p11_e4m3_ties_to_even_and_clamp():
     np.testing.assert_allclose(ofp8.quantize([3.0, 1000.0], 2.0), [3.0, 896.0])
 
 
+# ------------------------------------------------------------ P12 position interpolation
+def test_p12_pi_time_position_is_textbook_rope_at_fractional_position():
+    """t_scale s: the time pairs turn by (s t) theta^(-2j/d_t), the grid pairs as without PI
+    (textbook complex form at a fractional position; LoL review, PI baseline)."""
+    dims, grid_w = (44, 42, 42), 52
+    H, D, t, sc = 2, 128, 37, 0.3
+    b = orope.theta_hat(10000.0, 0.0, np.zeros(H))
+    x = RNG.standard_normal((1, 1560, H, D))
+    got = orope.rope3d_frame(x, t, b, dims, grid_w, t_scale=sc)
+    tok = np.arange(1560)
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    ang = []
+    for a, pos in enumerate([np.full(1560, t * sc), tok // grid_w, tok % grid_w]):
+        inv = 1.0 / (10000.0 ** (np.arange(0, dims[a], 2) / dims[a]))
+        ang.append(np.outer(pos, inv))
+    zr = z * np.exp(1j * np.concatenate(ang, axis=1))[None, :, None, :]
+    ref = np.empty_like(x)
+    ref[..., 0::2] = zr.real
+    ref[..., 1::2] = zr.imag
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(orope.rope3d_frame(x, t, b, dims, grid_w, t_scale=1.0),
+                                  orope.rope3d_frame(x, t, b, dims, grid_w))
+
+
+def test_p12_pi_compression_equals_stream_at_compressed_times():
+    """A stream with t_scale 1/4 fed frames at t = 4f (appends, attention and a recache) gives the
+    outputs of an uncompressed stream fed the same frames at t = f."""
+    bases, dims, grid = _tiny_setup(H=2, dims=(4, 2, 2), grid=(2, 2))
+    T, D, C = 4, 8, 6
+    q, k, v = (RNG.standard_normal((1, 6 * T, 2, D)) for _ in range(3))
+    x = RNG.standard_normal((1, 3 * T, C))
+    wk, wv = RNG.standard_normal((C, 2 * D)), RNG.standard_normal((C, 2 * D))
+    outs = []
+    for step, sc in ((1, 1.0), (4, 0.25)):
+        so = ostream.StreamOracle(1, 2, T, grid[1], dims, bases, t_scale=sc)
+        o = []
+        for f in range(6):
+            sl = slice(f * T, (f + 1) * T)
+            so.append(k[:, sl], v[:, sl], step * f)
+            if f == 3:
+                so.recache(x, wk, wv)
+            o.append(so.attend(q[:, sl], causal=True))
+        outs.append(np.concatenate(o, axis=1))
+    np.testing.assert_allclose(outs[1], outs[0], rtol=0, atol=1e-12)
+    # and it differs from the same t = 4f stream without PI
+    so = ostream.StreamOracle(1, 2, T, grid[1], dims, bases)
+    for f in range(2):
+        so.append(k[:, f * T:(f + 1) * T], v[:, f * T:(f + 1) * T], 4 * f)
+    assert np.abs(so.attend(q[:, T:2 * T], causal=True) - outs[0][:, T:2 * T]).max() > 1e-3
+
+
+def test_p12_pi_phase_coherence_scales_the_offset():
+    """C(Delta) under t_scale s is C(s Delta) without it; d_t = 2 gives exp(j s Delta)."""
+    eps = RNG.uniform(-1, 1, size=3)
+    bases = orope.theta_hat(10000.0, 0.8, eps)
+    deltas = np.array([0.0, 2.0, 10.0, 264.0, 402.0])
+    np.testing.assert_allclose(odiag.phase_coherence(bases, (44, 42, 42), deltas, t_scale=0.5),
+                               odiag.phase_coherence(bases, (44, 42, 42), deltas / 2), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(odiag.phase_coherence(bases, (2, 4, 2), deltas, t_scale=0.125),
+                               np.exp(1j * 0.125 * deltas)[None, :].repeat(3, 0), atol=1e-13)
+
+
 # ------------------------------------------------------------ P7 closed forms
 def test_p7_single_visible_key_returns_its_value():
     bases, dims, grid = _tiny_setup(H=2, dims=(4, 2, 2), grid=(1, 1))
