@@ -85,6 +85,10 @@ typedef enum { SA_MASK_NONE = 0, SA_MASK_FRAME_CAUSAL = 1 } sa_mask;
  * theta_hat_h on jittered axes (jitter_axes bitmask) and theta0 elsewhere.
  * Positions: t = the latent frame's time index; h = token / grid_w;
  * w = token % grid_w.
+ * [LoL] results, position-interpolation (PI) baseline: positions compressed
+ *   by a factor.  Here the time position becomes t * t_scale (grid positions
+ *   unchanged); the library folds t_scale into the time-axis frequencies, so
+ *   the angle is t * (w * t_scale).
  */
 typedef struct {
   int32_t n_heads;      /* H >= 1 */
@@ -95,13 +99,14 @@ typedef struct {
   double sigma;         /* jitter scale, >= 0; every theta_hat must stay > 1 */
   const double* eps;    /* host [H], each in [-1, 1]; NULL = no jitter; copied */
   uint32_t jitter_axes; /* SA_AXIS_* bitmask; 0 is treated as SA_AXIS_T */
+  double t_scale;       /* time-position scale (PI); 0 is treated as 1; else finite, > 0 */
 } sa_rope_desc;
 
 typedef struct sa_rope sa_rope;
 
 /* Host-only: per-head bases theta_hat [H*3] (t, h, w) and frequencies
- * w [H*D/2] in fp64, as the device tables will hold them.  No HIP call; either
- * output may be NULL. */
+ * w [H*D/2] in fp64, as the device tables will hold them (time-axis entries
+ * multiplied by t_scale).  No HIP call; either output may be NULL. */
 sa_status sa_rope_tables(const sa_rope_desc* desc, double* theta_hat_out, double* freq_out);
 
 /* Validates desc, builds the fp64 frequency table and the cos/sin table of
@@ -258,7 +263,8 @@ sa_status sa_window_attn_sink_mass(const sa_cache* cache, const void* q, void* o
 /* Phase-coherence kernel per head ([LoL] "core innovation" paragraph), on the
  * host in fp64, from the same tables sa_rope_create builds:
  *   C_h(delta) = (1/K) sum_{i<K} exp(j w_{h,t,i} delta)
- * over head h's K = dim_t/2 time-axis frequencies, delta a frame offset.
+ * over head h's K = dim_t/2 time-axis frequencies, delta a frame offset
+ * (with t_scale, a time-position offset of delta * t_scale).
  *   deltas [n] host; re, im [n_heads][n] host.  No HIP call.
  * SA_ERR_SHAPE if dim_t is 0. */
 sa_status sa_rope_phase_coherence(const sa_rope_desc* desc, const double* deltas, int32_t n, double* re,

@@ -37,7 +37,8 @@ class sa_rope_desc(ctypes.Structure):
                 ("dim_t", ctypes.c_int32), ("dim_h", ctypes.c_int32), ("dim_w", ctypes.c_int32),
                 ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
                 ("theta0", ctypes.c_double), ("sigma", ctypes.c_double),
-                ("eps", ctypes.POINTER(ctypes.c_double)), ("jitter_axes", ctypes.c_uint32)]
+                ("eps", ctypes.POINTER(ctypes.c_double)), ("jitter_axes", ctypes.c_uint32),
+                ("t_scale", ctypes.c_double)]
 
 
 class sa_cache_desc(ctypes.Structure):
@@ -139,7 +140,7 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes):
+def _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale=1.0):
     d = sa_rope_desc()
     d.n_heads, d.head_dim = n_heads, head_dim
     d.dim_t, d.dim_h, d.dim_w = dims
@@ -150,13 +151,14 @@ def _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes):
         keep = (ctypes.c_double * n_heads)(*[float(e) for e in eps])
         d.eps = ctypes.cast(keep, ctypes.POINTER(ctypes.c_double))
     d.jitter_axes = jitter_axes
+    d.t_scale = float(t_scale)
     return d, keep
 
 
 def sa_rope_tables(n_heads, head_dim, dims, grid, theta0=10000.0, sigma=0.0, eps=None,
-                   jitter_axes=SA_AXIS_T):
+                   jitter_axes=SA_AXIS_T, t_scale=1.0):
     """Host-only tables: (theta_hat [H][3], freq [H][D/2]) as nested lists of floats."""
-    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes)
+    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale)
     th = (ctypes.c_double * (n_heads * 3))()
     fr = (ctypes.c_double * (n_heads * head_dim // 2))()
     _check(lib().sa_rope_tables(ctypes.byref(d), th, fr), "sa_rope_tables")
@@ -168,9 +170,9 @@ class Rope:
     """Owns an sa_rope handle (per-head fp64 frequency table on the device)."""
 
     def __init__(self, n_heads, head_dim, dims, grid, theta0=10000.0, sigma=0.0, eps=None,
-                 jitter_axes=SA_AXIS_T):
+                 jitter_axes=SA_AXIS_T, t_scale=1.0):
         self.n_heads, self.head_dim, self.dims, self.grid = n_heads, head_dim, tuple(dims), tuple(grid)
-        d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes)
+        d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale)
         h = _VP()
         _check(lib().sa_rope_create(ctypes.byref(d), ctypes.byref(h)), "sa_rope_create")
         self.handle = h
@@ -293,9 +295,9 @@ def sa_window_attn_sink_mass(cache: Cache, q, o, sink_mass, n_q: int, scale: flo
 
 
 def sa_rope_phase_coherence(n_heads, head_dim, dims, grid, deltas: Sequence[float], theta0=10000.0, sigma=0.0,
-                            eps=None, jitter_axes=SA_AXIS_T):
+                            eps=None, jitter_axes=SA_AXIS_T, t_scale=1.0):
     """Host-only C_h(delta) over each head's time-axis frequencies: list (per head) of complex values."""
-    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes)
+    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale)
     n = len(deltas)
     dl = (ctypes.c_double * max(n, 1))(*[float(x) for x in deltas])
     re = (ctypes.c_double * max(n_heads * n, 1))()

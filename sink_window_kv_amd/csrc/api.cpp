@@ -79,6 +79,8 @@ sa_status check_rope_desc(const sa_rope_desc* d) {
   if (!(d->theta0 > 1.0) || !std::isfinite(d->theta0)) return fail(SA_ERR_RANGE, "theta0 must be finite and > 1");
   if (!(d->sigma >= 0.0) || !std::isfinite(d->sigma)) return fail(SA_ERR_RANGE, "sigma must be finite and >= 0");
   if (d->jitter_axes > 7u) return fail(SA_ERR_RANGE, "jitter_axes must be a SA_AXIS_* mask");
+  if (d->t_scale != 0.0 && !(d->t_scale > 0.0 && std::isfinite(d->t_scale)))
+    return fail(SA_ERR_RANGE, "t_scale must be 0 (none) or finite and > 0");
   if (d->eps) {
     for (int h = 0; h < d->n_heads; ++h) {
       const double e = d->eps[h];
@@ -227,7 +229,7 @@ sa_status sa_rope_tables(const sa_rope_desc* desc, double* theta_hat_out, double
   if (sa_status s = check_rope_desc(desc)) return s;
   const int dims[3] = {desc->dim_t, desc->dim_h, desc->dim_w};
   const sa::RopeTables t = sa::build_rope_tables(desc->n_heads, desc->head_dim, dims, desc->theta0,
-                                                 desc->sigma, desc->eps, desc->jitter_axes);
+                                                 desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale);
   if (theta_hat_out) std::memcpy(theta_hat_out, t.theta_hat.data(), t.theta_hat.size() * sizeof(double));
   if (freq_out) std::memcpy(freq_out, t.freq.data(), t.freq.size() * sizeof(double));
   return ok();
@@ -240,7 +242,7 @@ sa_status sa_rope_phase_coherence(const sa_rope_desc* desc, const double* deltas
   if (desc->dim_t == 0) return fail(SA_ERR_SHAPE, "no time-axis channels (dim_t is 0)");
   const int dims[3] = {desc->dim_t, desc->dim_h, desc->dim_w};
   const sa::RopeTables t = sa::build_rope_tables(desc->n_heads, desc->head_dim, dims, desc->theta0,
-                                                 desc->sigma, desc->eps, desc->jitter_axes);
+                                                 desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale);
   const int half = desc->head_dim / 2;
   const int K = desc->dim_t / 2;  // time pairs come first in every head's table
   for (int h = 0; h < desc->n_heads; ++h)
@@ -270,7 +272,7 @@ sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out) {
   r->grid_h = desc->grid_h;
   r->grid_w = desc->grid_w;
   r->tables = sa::build_rope_tables(desc->n_heads, desc->head_dim, r->dims, desc->theta0,
-                                    desc->sigma, desc->eps, desc->jitter_axes);
+                                    desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale);
   r->grid_table = sa::build_rope_grid_table(r->tables, desc->n_heads, desc->head_dim, r->dims, desc->grid_h,
                                             desc->grid_w, desc->jitter_axes);
   hipError_t e = hipGetDevice(&r->device);

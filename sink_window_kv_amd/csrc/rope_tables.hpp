@@ -20,9 +20,13 @@ struct RopeTables {
   std::vector<double> freq;       // [H][D/2]
 };
 
+// t_scale: position interpolation on the time axis (LoL review, PI baseline),
+// folded into the time-axis frequencies: angle t * (w * t_scale).
 inline RopeTables build_rope_tables(int n_heads, int head_dim, const int dims[3], double theta0,
-                                    double sigma, const double* eps, uint32_t jitter_axes) {
+                                    double sigma, const double* eps, uint32_t jitter_axes,
+                                    double t_scale = 1.0) {
   if (jitter_axes == 0) jitter_axes = 1u;
+  if (t_scale == 0.0) t_scale = 1.0;
   RopeTables t;
   t.theta_hat.resize(static_cast<size_t>(n_heads) * 3);
   t.freq.resize(static_cast<size_t>(n_heads) * (head_dim / 2));
@@ -38,7 +42,7 @@ inline RopeTables build_rope_tables(int n_heads, int head_dim, const int dims[3]
       for (int j = 0; j < dims[a] / 2; ++j, ++p) {
         // base^(-2j/d_a); j = 0 gives exactly 1.
         t.freq[static_cast<size_t>(h) * (head_dim / 2) + p] =
-            std::pow(base, -2.0 * static_cast<double>(j) / static_cast<double>(dims[a]));
+            std::pow(base, -2.0 * static_cast<double>(j) / static_cast<double>(dims[a])) * (a == 0 ? t_scale : 1.0);
       }
     }
   }

@@ -47,17 +47,17 @@ def _env(**kv):
 class GpuStream:
     """Drives one layer's cache through the C-ABI and mirrors it in the oracle."""
 
-    def __init__(self, w, layer=0, eps=None, with_oracle=True):
+    def __init__(self, w, layer=0, eps=None, with_oracle=True, t_scale=1.0):
         import torch
         swk = _swk()
         self.w = w
         self.eps = eps
-        self.rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid, w.theta0, w.sigma, eps)
+        self.rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid, w.theta0, w.sigma, eps, t_scale=t_scale)
         self.cache = swk.Cache(self.rope, w.batch, w.n_sink, w.n_local, torch_dtype(w.dtype))
         bases = orope.theta_hat(w.theta0, w.sigma, eps if eps is not None else np.zeros(w.n_heads))
         self.bases = bases
         self.oracle = ostream.StreamOracle(w.n_sink, w.n_local, w.tokens_per_frame, w.grid[1], w.dims,
-                                           bases) if with_oracle else None
+                                           bases, t_scale=t_scale) if with_oracle else None
 
     def append(self, k, v, n, t0):
         _swk().sa_cache_append(self.cache, to_dev(k, self.w.dtype), to_dev(v, self.w.dtype), n, t0)
@@ -135,6 +135,43 @@ def test_window_size_variants_wan_layer(n_sink, n_local):
         if f in check:
             o = gs.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
             _check(gs, q, o, True, rows=rows, what=f"window {n_sink}+{n_local} frame {f}")
+
+
+def test_position_interpolation_wan_layer():
+    """Position interpolation (LoL review's PI baseline): time positions t * 1/4 with LoL jitter at the
+    Wan-1.3B layer shapes.  Frames appended at t = 4f: sampled rows match the oracle at fractional
+    positions, and every output is bit-identical to a stream without PI fed the same frames at t = f
+    (w/4 is exact in fp64, so the device angles are the same numbers)."""
+    import torch
+    swk = _swk()
+    w = wl.WORKLOADS[3]
+    eps = wl.head_jitter(w)
+    pi = GpuStream(w, eps=eps, t_scale=0.25)
+    plain = GpuStream(w, eps=eps, with_oracle=False)
+    rows = sample_rows(w.tokens_per_frame, w.tokens_per_frame, n=48, seed=11)
+    for f in range(14):
+        q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=None if t == wl.TENSOR_V else 1.0)
+                   for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+        pi.append(k, v, 1, 4 * f)
+        plain.append(k, v, 1, f)
+        o_pi = pi.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
+        o_plain = plain.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
+        assert torch.equal(o_pi, o_plain), f"frame {f}: PI at t = 4f differs from t = f"
+        if f in (0, 2, 13):
+            _check(pi, q, o_pi, True, rows=rows, what=f"PI 1/4 frame {f} (t = {4 * f})")
+
+
+def test_position_interpolation_f32_fractional():
+    """fp32 stream with t_scale 1/3 (positions not representable exactly) and a large time offset:
+    every row of every frame at 1e-5."""
+    swk = _swk()
+    w = wl.WORKLOADS[1]
+    gs = GpuStream(w, t_scale=1.0 / 3.0)
+    for f in range(w.frames):
+        q, k, v = (wl.frame_qkv(w, f, tensor=t) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+        gs.append(k, v, 1, 1000 + 7 * f)
+        o = gs.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
+        _check(gs, q, o, True, what=f"PI 1/3 f32 frame {f}")
 
 
 def test_cfg2_unscaled_scores_and_custom_scale():

@@ -43,6 +43,25 @@ def test_rope3d_apply_matches_oracle(cfg, t0, n_frames):
     assert torch.equal(tx, ty)
 
 
+@pytest.mark.parametrize("cfg,t0,t_scale", [(1, 5, 0.125), (3, 1198, 0.3), (3, 100000, 1.0 / 3.0)])
+def test_rope3d_apply_position_interpolation(cfg, t0, t_scale):
+    """Time positions t * t_scale (LoL review's PI baseline) against the oracle at fractional positions."""
+    import torch
+    swk = _swk()
+    w = wl.WORKLOADS[cfg]
+    eps = wl.head_jitter(w) if w.sigma > 0 else None
+    rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid, w.theta0, w.sigma, eps, t_scale=t_scale)
+    x = wl.chunk_qkv(w, 0, 2, tensor=wl.TENSOR_K, scale=1.0)
+    tx = to_dev(x, w.dtype)
+    ty = torch.empty_like(tx)
+    swk.sa_rope3d_apply(rope, tx, ty, w.batch, 2, t0)
+    torch.cuda.synchronize()
+    bases = orope.theta_hat(w.theta0, w.sigma, eps if eps is not None else np.zeros(w.n_heads))
+    ref = orope.rope3d(x, t0, w.tokens_per_frame, bases, w.dims, w.grid[1], t_scale=t_scale)
+    rel, mx = assert_close(to_np(ty), ref, w.dtype, f"rope PI cfg{cfg}")
+    log(f"  PI {t_scale:.3f} cfg{cfg} t0={t0}: rel_l2 {rel:.2e} max_abs {mx:.2e}")
+
+
 def test_rope_all_axes_jittered_and_host_tables():
     """Host tables equal the oracle's theta_hat/frequencies; all-axis jitter parity on device."""
     import torch

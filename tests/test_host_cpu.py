@@ -64,7 +64,27 @@ def test_host_phase_coherence_matches_oracle(sigma, axes, names, dims):
     assert e.value.status == swk.SA_ERR_SHAPE
 
 
+@pytest.mark.parametrize("t_scale", [0.25, 0.1, 3.0])
+def test_host_position_interpolation_tables_and_coherence(t_scale):
+    """t_scale scales the time-axis frequencies only; C(delta) equals the oracle's under PI; 0 means 1."""
+    swk = _swk()
+    eps = np.random.default_rng(4).uniform(-1, 1, 12)
+    dims = (44, 42, 42)
+    _, fr = swk.sa_rope_tables(12, 128, dims, (30, 52), 10000.0, 0.8, eps, 1, t_scale)
+    bases = orope.theta_hat(10000.0, 0.8, eps)
+    for h in range(12):
+        ref = orope.head_frequencies(bases[h], dims)
+        ref[:dims[0] // 2] *= t_scale
+        np.testing.assert_allclose(fr[h], ref, rtol=1e-14)
+    assert swk.sa_rope_tables(12, 128, dims, (30, 52), 10000.0, 0.8, eps, 1, 0.0) == \
+        swk.sa_rope_tables(12, 128, dims, (30, 52), 10000.0, 0.8, eps, 1)
+    deltas = [0, 1, 3, 132, 201, 1200]
+    got = np.array(swk.sa_rope_phase_coherence(12, 128, dims, (30, 52), deltas, 10000.0, 0.8, eps, 1, t_scale))
+    np.testing.assert_allclose(got, odiag.phase_coherence(bases, dims, deltas, t_scale=t_scale), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("kw,status", [
+    (dict(t_scale=-0.5), 6), (dict(t_scale=float("inf")), 6), (dict(t_scale=float("nan")), 6),
     (dict(head_dim=96), 2), (dict(dims=(44, 42, 40)), 2), (dict(dims=(43, 43, 42)), 2),
     (dict(grid=(3, 3)), 2), (dict(theta0=1.0), 6), (dict(sigma=-0.1), 6),
     (dict(eps=[1.5] * 12), 6), (dict(sigma=1.0, eps=[-1.0] * 12), 6), (dict(jitter_axes=8), 6),
