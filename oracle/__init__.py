@@ -29,6 +29,9 @@ float64, written from the pages:
                    method" and "core innovation" paragraphs).
 * ``fp8``       -- e4m3 rounding of the FP8 cache (OCP 8-bit float, the
                    format the reviewed model card's FP8 variant is read as).
+* ``quant``     -- row-wise 8-bit quantisation (int8, e4m3) and the W8A8
+                   product of the 8-bit projections (LongLive paper review,
+                   "INT8 quantized inference" table; model card FP8 variant).
 * ``brute``     -- pure-Python loop versions for tiny shapes, used to pin the
                    numpy versions.
 * ``stream``    -- composes the above into the per-frame stream the library
@@ -37,4 +40,4 @@ float64, written from the pages:
 Pins (tests/test_oracle_*.py) tie these to closed forms, invariants,
 library routines and brute force; see the test docstrings.
 """
-from . import rope, cache, attention, recache, project, brute, stream, diagnostics, fp8  # noqa: F401
+from . import rope, cache, attention, recache, project, brute, stream, diagnostics, fp8, quant  # noqa: F401

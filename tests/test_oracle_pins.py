@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from oracle import attention as oattn
-from oracle import brute, cache as ocache, diagnostics as odiag, fp8 as ofp8, project as oproject, recache as orecache, rope as orope, stream as ostream
+from oracle import brute, cache as ocache, diagnostics as odiag, fp8 as ofp8, project as oproject, quant as oquant, recache as orecache, rope as orope, stream as ostream
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(1234)
@@ -500,6 +500,63 @@ def test_p12_pi_phase_coherence_scales_the_offset():
                                odiag.phase_coherence(bases, (44, 42, 42), deltas / 2), rtol=0, atol=1e-13)
     np.testing.assert_allclose(odiag.phase_coherence(bases, (2, 4, 2), deltas, t_scale=0.125),
                                np.exp(1j * 0.125 * deltas)[None, :].repeat(3, 0), atol=1e-13)
+
+
+# ------------------------------------------------------------ P13 8-bit projections
+def test_p13_int8_rows_closed_forms():
+    """Row max 127 gives scale 1 and codes = x rounded half to even; max 2 gives inv 63.5 (1 -> 63.5 -> 64);
+    a zero row gives scale 0 and codes 0; the largest magnitude maps to +-127 exactly."""
+    x = np.array([[127.0, 2.5, -3.5, 0.5, -127.0, 1.49], [2.0, 1.0, -0.5, 0.0, -2.0, 0.25], [0.0] * 6])
+    c, sc = oquant.quantize_rows(x, "int8")
+    assert c.dtype == np.int8 and sc.dtype == np.float32
+    np.testing.assert_array_equal(c[0], [127, 2, -4, 0, -127, 1])
+    np.testing.assert_array_equal(c[1], [127, 64, -32, 0, -127, 16])
+    np.testing.assert_array_equal(c[2], 0)
+    np.testing.assert_array_equal(sc, np.float32([1.0, 2.0 / 127.0, 0.0]))
+    xr = RNG.standard_normal((40, 96)).astype(np.float32) * np.float32(3.0)
+    c, sc = oquant.quantize_rows(xr, "int8")
+    np.testing.assert_array_equal(np.abs(c).max(axis=1), 127)
+    err = np.abs(xr - oquant.dequantize(c, sc, "int8"))
+    assert np.all(err <= sc[:, None].astype(np.float64) * (0.5 + 1e-5))
+
+
+def test_p13_e4m3_rows_and_codes():
+    """Every finite e4m3 code encodes back to itself (zeros keep their sign); a row with max 448 keeps its
+    values rounded to e4m3 (448 -> 0x7e, 1 -> 0x38, -3 -> 0xc4); scaled rows put their max at 448 and
+    stay within half an e4m3 step."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    np.testing.assert_array_equal(oquant.e4m3_encode(ofp8.decode(codes)), codes)
+    c, sc = oquant.quantize_rows(np.array([[448.0, 1.0, -3.0, 0.1, -1e-6]]), "e4m3")
+    np.testing.assert_array_equal(c[0], [0x7E, 0x38, 0xC4, oquant.e4m3_encode(ofp8.round_e4m3(0.1)), 0x80])
+    assert sc[0] == 1.0
+    xr = RNG.standard_normal((30, 64)).astype(np.float32)
+    c, sc = oquant.quantize_rows(xr, "e4m3")
+    np.testing.assert_array_equal(np.abs(ofp8.decode(c)).max(axis=1), 448.0)
+    y = xr.astype(np.float64) / sc[:, None]
+    err = np.abs(y - ofp8.decode(c))
+    assert np.all(err <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-5))
+
+
+@pytest.mark.parametrize("qtype", ["int8", "e4m3"])
+def test_p13_linear_q8_brute_force(qtype):
+    """The W8A8 product equals brute-force loops over the codes (x rows times weight rows, scales per
+    x row and per weight row); for int8 the fp32 recipe is within 3 fp32 roundings of the exact value."""
+    n, C, F = 5, 12, 7
+    cx, sx = oquant.quantize_rows(RNG.standard_normal((n, C)), qtype)
+    cw, sw = oquant.quantize_rows(RNG.standard_normal((F, C)) * 0.1, qtype)
+    got = oquant.linear_q8(cx, sx, cw, sw, qtype)
+    vx, vw = oquant.decode(cx, qtype), oquant.decode(cw, qtype)
+    for i in range(n):
+        for f in range(F):
+            acc = 0.0
+            for c in range(C):
+                acc += float(vx[i, c]) * float(vw[f, c])
+            ref = acc * float(sx[i]) * float(sw[f])
+            assert abs(float(got[i, f]) - ref) <= 4 * 2.0 ** -24 * abs(ref) + 1e-30, (i, f)
+    if qtype == "int8":
+        assert got.dtype == np.float32
+        acc = sum(int(cx[1, c]) * int(cw[2, c]) for c in range(C))
+        assert got[1, 2] == (np.float32(acc) * sx[1]) * sw[2]
 
 
 # ------------------------------------------------------------ P7 closed forms
