@@ -442,6 +442,55 @@ def main():
           f"append {p8 * 1e3:.1f} us; B=4 chunks {a58 * 1e3:.1f} us ({flops5 / (a58 * 1e-3) / 1e12:.0f} TFLOP/s)",
           file=sys.stderr, flush=True)
 
+    # 8-bit projections (W8A8: int8 or e4m3 codes, fp32 scales per token and
+    # per output feature): row quantisation of one frame's hidden states, the
+    # output projection, the fused q/k/v projections + append, and the recache.
+    q8 = {"workload": "W8A8 projections: codes with one fp32 scale per token (x) and per output feature (W); "
+                      "frame shapes of the layer block and the recache (x [18720 x 1536] -> K, V)"}
+    qx_bytes = T * C * 3 + T * 4
+    def q8_codes(t2d, qt):
+        cc = torch.empty(t2d.shape, dtype=torch.uint8, device=dev)
+        sc = torch.empty(t2d.shape[0], dtype=torch.float32, device=dev)
+        swk.sa_quantize_rows(t2d, cc, sc, qt)
+        return cc, sc
+    def timed(fn, n, warm=3):
+        for _ in range(warm):
+            fn()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    for qname, qt in (("int8", swk.SA_Q_INT8), ("e4m3", swk.SA_Q_E4M3)):
+        x0 = xs[0].reshape(T, C)
+        cx0 = torch.empty((T, C), dtype=torch.uint8, device=dev)
+        sx0 = torch.empty(T, dtype=torch.float32, device=dev)
+        quant_us = timed(lambda: swk.sa_quantize_rows(x0, cx0, sx0, qt), 50)
+        cq, sq = q8_codes(dqw, qt)
+        ck_, sk_ = q8_codes(dkw, qt)
+        cv_, sv_ = q8_codes(dvw, qt)
+        co_, so_ = q8_codes(dow, qt)
+        out_us = timed(lambda: swk.sa_linear_q8(cx0, sx0, co_, so_, yb, qt, T, C, C), 50)
+        cq8 = swk.Cache(rope, 1, w.n_sink, w.n_local, bf, device=dev)
+        tq8 = [0]
+        def pa():
+            swk.sa_cache_project_append_q8(cq8, cx0, sx0, cq, sq, ck_, sk_, cv_, sv_, qt, C, qb, 1, tq8[0])
+            tq8[0] += 1
+        pa_us = timed(pa, 40, warm=n_win)
+        cq8.close()
+        cxr, sxr = q8_codes(tx.reshape(-1, C), qt)
+        rc_q8_us = timed(lambda: swk.sa_cache_recache_q8(rc, cxr, sxr, ck_, sk_, cv_, sv_, qt, C), 10)
+        q8[qname] = {"quantize_frame_us": round(quant_us, 2),
+                     "quantize_GBps": round(qx_bytes / (quant_us * 1e-6) / 1e9, 1),
+                     "out_proj_us": round(out_us, 1), "out_proj_TOPs": round(op_flops / (out_us * 1e-6) / 1e12, 1),
+                     "qkv_append_us": round(pa_us, 1), "qkv_TOPs": round(pj_flops / (pa_us * 1e-6) / 1e12, 1),
+                     "recache_us": round(rc_q8_us, 1), "recache_TOPs": round(rc_flops / (rc_q8_us * 1e-6) / 1e12, 1),
+                     "recache_pct_8bit_peak": round(100.0 * rc_flops / (rc_q8_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 2)}
+        print(f"[bench] {qname} projections: quantize {quant_us:.1f} us, output projection {out_us:.1f} us, "
+              f"q/k/v + append {pa_us:.1f} us, recache {rc_q8_us:.1f} us "
+              f"({rc_flops / (rc_q8_us * 1e-6) / 1e12:.0f} TOP/s)", file=sys.stderr, flush=True)
+
     traffic = traffic_from_profile(ATTN_BF16_SOURCES)
     out = {
         "metric": "sink+window attn TFLOP/s & latent frames/s/layer on 1 MI355X; % bf16 MFMA peak",
@@ -508,6 +557,7 @@ def main():
                       "latent_frames_per_s_per_layer": round(1e3 / (a8 + p8), 1),
                       "b4_chunk_attention_avg_us": round(a58 * 1e3, 1),
                       "b4_chunk_TFLOPs": round(flops5 / (a58 * 1e-3) / 1e12, 1)},
+        "q8_projections": q8,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

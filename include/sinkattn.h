@@ -228,6 +228,56 @@ sa_status sa_cache_project_append(sa_cache* cache, const void* x, const void* w_
 sa_status sa_linear(const void* x, const void* w, void* y, sa_dtype dtype, int64_t n_rows,
                     int32_t in_features, int32_t out_features, void* stream);
 
+/* ----------------------------------------------------- 8-bit projections --
+ * [LongLive] "INT8 quantized inference" table (the INT8 model: half the
+ * size, 12.6 -> 16.4 FPS) and [LongLive model card] FP8 variant (24.8 FPS);
+ * neither gives a scheme.  Here (W8A8) both operands of a projection are
+ * 8-bit codes with one fp32 scale per row -- per token for x [n][C], per
+ * output feature for W [F][C] ([out, in] layout):
+ *   y[n][f] = bf16( (float(sum_c qx[n][c] qw[f][c]) * sx[n]) * sw[f] )
+ * Codes are int8 (|q| <= 127; the sum is exact in int32) or OCP e4m3 (the
+ * products are exact, summed in fp32).  bf16 rounding is to nearest even.
+ * Every buffer is a device pointer, 16-byte aligned.
+ */
+typedef enum { SA_Q_INT8 = 0, SA_Q_E4M3 = 1 } sa_qtype;
+
+/* Row-wise quantisation, every step in fp32: a = max_c |x[r][c]|,
+ * scales[r] = a / Q, codes[r][c] = round(x[r][c] * (Q / a)) with Q = 127
+ * (int8: nearest, ties to even) or 448 (e4m3: nearest even); a row of zeros
+ * gets scale 0 and codes 0.  Serves activations (per token) and weights
+ * [F][C] (per output feature) alike.
+ *   x [n_rows, n_cols] bf16 (finite); codes [n_rows, n_cols] bytes (int8 or
+ *   e4m3); scales [n_rows] fp32.  n_cols a multiple of 8 in [8, 65536];
+ *   n_rows >= 0 (0 launches nothing). */
+sa_status sa_quantize_rows(const void* x, void* codes, float* scales, sa_qtype qtype, int64_t n_rows,
+                           int32_t n_cols, void* stream);
+
+/* Plain W8A8 linear map: x codes [n_rows, in_features] with scales [n_rows],
+ * w codes [out_features, in_features] with scales [out_features]; y
+ * [n_rows, out_features] bf16 as above.  in_features a multiple of 64 in
+ * [64, 65536], out_features a multiple of 16; y must not overlap the
+ * inputs. */
+sa_status sa_linear_q8(const void* x_codes, const float* x_scales, const void* w_codes,
+                       const float* w_scales, void* y, sa_qtype qtype, int64_t n_rows,
+                       int32_t in_features, int32_t out_features, void* stream);
+
+/* sa_cache_recache with 8-bit operands: x codes [B*n_res*T_f, hidden]
+ * (logical order, one scale per token), w_k / w_v codes [H*D, hidden] (one
+ * scale per output feature).  The cache (SA_BF16 or SA_FP8) receives the
+ * bf16-rounded products as in sa_cache_recache.  hidden a multiple of 64. */
+sa_status sa_cache_recache_q8(sa_cache* cache, const void* x_codes, const float* x_scales,
+                              const void* wk_codes, const float* wk_scales, const void* wv_codes,
+                              const float* wv_scales, sa_qtype qtype, int32_t hidden, void* stream);
+
+/* sa_cache_project_append with 8-bit operands (x codes one scale per token,
+ * weights one scale per output feature); wq_codes, wq_scales and q_out
+ * (bf16) are given together or all NULL.  hidden a multiple of 64. */
+sa_status sa_cache_project_append_q8(sa_cache* cache, const void* x_codes, const float* x_scales,
+                                     const void* wq_codes, const float* wq_scales, const void* wk_codes,
+                                     const float* wk_scales, const void* wv_codes, const float* wv_scales,
+                                     sa_qtype qtype, int32_t hidden, void* q_out, int32_t n_frames,
+                                     int64_t t0, void* stream);
+
 /* Workspace sa_window_attn needs for this cache state and n_q (may be 0). */
 sa_status sa_window_attn_workspace(const sa_cache* cache, int32_t n_q, size_t* bytes);
 

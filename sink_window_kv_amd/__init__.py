@@ -19,6 +19,7 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_ALIGN, SA_ERR_STATE, SA_E
 SA_BF16, SA_F32, SA_FP8 = 0, 1, 2
 SA_MASK_NONE, SA_MASK_FRAME_CAUSAL = 0, 1
 SA_AXIS_T, SA_AXIS_H, SA_AXIS_W = 1, 2, 4
+SA_Q_INT8, SA_Q_E4M3 = 0, 1
 SA_MAX_FRAMES = 64
 
 
@@ -70,6 +71,12 @@ _SIGNATURES = {
     "sa_cache_project_append": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_int32, _VP, ctypes.c_int32,
                                                ctypes.c_int64, _VP]),
     "sa_linear": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _VP]),
+    "sa_quantize_rows": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _VP]),
+    "sa_linear_q8": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_int32, _VP]),
+    "sa_cache_recache_q8": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int, ctypes.c_int32, _VP]),
+    "sa_cache_project_append_q8": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int,
+                                                  ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int64, _VP]),
     "sa_window_attn_sink_mass": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
                                                 _VP, ctypes.c_size_t, _VP]),
     "sa_rope_phase_coherence": (ctypes.c_int, [ctypes.POINTER(sa_rope_desc), ctypes.POINTER(ctypes.c_double),
@@ -271,6 +278,37 @@ def sa_linear(x, w, y, n_rows: int, in_features: int, out_features: int, stream=
     """y [n_rows, out] = x [n_rows, in] . w^T, w in the [out, in] layout."""
     _check(lib().sa_linear(_ptr(x), _ptr(w), _ptr(y), _dtype_code(x), n_rows, in_features, out_features,
                            _stream(stream)), "sa_linear")
+
+
+def sa_quantize_rows(x, codes, scales, qtype: int, stream=None):
+    """Row-wise 8-bit codes of x [n_rows, n_cols] bf16: codes (int8 / uint8 bytes) same shape, scales [n_rows] fp32."""
+    n_rows, n_cols = (x.shape[0], x.shape[1]) if x.dim() == 2 else (x.numel() // x.shape[-1], x.shape[-1])
+    _check(lib().sa_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), qtype, n_rows, n_cols, _stream(stream)),
+           "sa_quantize_rows")
+
+
+def sa_linear_q8(x_codes, x_scales, w_codes, w_scales, y, qtype: int, n_rows: int, in_features: int,
+                 out_features: int, stream=None):
+    """y [n_rows, out] bf16 = (float(x_codes . w_codes^T) * x_scales[row]) * w_scales[feature]."""
+    _check(lib().sa_linear_q8(_ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales), _ptr(y), qtype, n_rows,
+                              in_features, out_features, _stream(stream)), "sa_linear_q8")
+
+
+def sa_cache_recache_q8(cache: Cache, x_codes, x_scales, wk_codes, wk_scales, wv_codes, wv_scales, qtype: int,
+                        hidden: int, stream=None):
+    """sa_cache_recache with 8-bit operands (scales per token and per output feature)."""
+    _check(lib().sa_cache_recache_q8(cache.handle, _ptr(x_codes), _ptr(x_scales), _ptr(wk_codes), _ptr(wk_scales),
+                                     _ptr(wv_codes), _ptr(wv_scales), qtype, hidden, _stream(stream)),
+           "sa_cache_recache_q8")
+
+
+def sa_cache_project_append_q8(cache: Cache, x_codes, x_scales, wq_codes, wq_scales, wk_codes, wk_scales, wv_codes,
+                               wv_scales, qtype: int, hidden: int, q_out, n_frames: int, t0: int, stream=None):
+    """sa_cache_project_append with 8-bit operands; wq_codes, wq_scales and q_out may all be None."""
+    _check(lib().sa_cache_project_append_q8(cache.handle, _ptr(x_codes), _ptr(x_scales), _ptr(wq_codes),
+                                            _ptr(wq_scales), _ptr(wk_codes), _ptr(wk_scales), _ptr(wv_codes),
+                                            _ptr(wv_scales), qtype, hidden, _ptr(q_out), n_frames, t0,
+                                            _stream(stream)), "sa_cache_project_append_q8")
 
 
 def sa_window_attn_workspace(cache: Cache, n_q: int) -> int:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ["api.cpp", "rope_append.hip", "window_attn.hip", "window_attn_fp8.hip", "proj_gemm.hip"]
+SOURCES = ["api.cpp", "rope_append.hip", "window_attn.hip", "window_attn_fp8.hip", "proj_gemm.hip", "quantize.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -450,6 +450,144 @@ sa_status sa_linear(const void* x, const void* w, void* y, sa_dtype dtype, int64
   return ok();
 }
 
+static sa_status q8_op(sa_qtype qtype, int* op) {
+  if (qtype == SA_Q_INT8) *op = sa::kOpI8;
+  else if (qtype == SA_Q_E4M3) *op = sa::kOpE4M3;
+  else return fail(SA_ERR_DTYPE, "qtype must be SA_Q_INT8 or SA_Q_E4M3");
+  return SA_OK;
+}
+
+// 8-bit GEMM operands: slices of 64 codes.
+static sa_status check_q8_hidden(int32_t hidden) {
+  if (hidden < 64 || hidden % 64 != 0 || hidden > (1 << 16))
+    return fail(SA_ERR_SHAPE, "hidden / in_features must be a multiple of 64 in [64, 65536] for 8-bit operands");
+  return SA_OK;
+}
+
+sa_status sa_quantize_rows(const void* x, void* codes, float* scales, sa_qtype qtype, int64_t n_rows, int32_t n_cols,
+                           void* stream) {
+  if (!x || !codes || !scales) return fail(SA_ERR_NULL, "x, codes and scales must be non-NULL");
+  int op = 0;
+  if (sa_status s = q8_op(qtype, &op)) return s;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(SA_ERR_ALIGN, "x, codes and scales must be 16-byte aligned");
+  if (n_rows < 0) return fail(SA_ERR_SHAPE, "n_rows must be >= 0");
+  if (n_cols < 8 || n_cols % 8 != 0 || n_cols > (1 << 16))
+    return fail(SA_ERR_SHAPE, "n_cols must be a multiple of 8 in [8, 65536]");
+  const hipError_t e = sa::launch_quantize_rows(x, codes, scales, op, n_rows, n_cols, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return ok();
+}
+
+sa_status sa_linear_q8(const void* x_codes, const float* x_scales, const void* w_codes, const float* w_scales, void* y,
+                       sa_qtype qtype, int64_t n_rows, int32_t in_features, int32_t out_features, void* stream) {
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !y)
+    return fail(SA_ERR_NULL, "codes, scales and y must be non-NULL");
+  int op = 0;
+  if (sa_status s = q8_op(qtype, &op)) return s;
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y))
+    return fail(SA_ERR_ALIGN, "codes, scales and y must be 16-byte aligned");
+  if (n_rows < 0) return fail(SA_ERR_SHAPE, "n_rows must be >= 0");
+  if (out_features < 16 || out_features % 16 != 0 || out_features > (1 << 20))
+    return fail(SA_ERR_SHAPE, "out_features must be a multiple of 16 in [16, 2^20]");
+  if (sa_status s = check_q8_hidden(in_features)) return s;
+  if (sa_status s = check_proj_sizes(n_rows, in_features, out_features, 1)) return s;
+  const auto overlaps = [](const void* p, size_t pb, const void* q, size_t qb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+    return a0 < b0 + qb && b0 < a0 + pb;
+  };
+  const size_t yb = static_cast<size_t>(n_rows) * out_features * 2;
+  if (n_rows > 0 && (overlaps(y, yb, x_codes, static_cast<size_t>(n_rows) * in_features) ||
+                     overlaps(y, yb, w_codes, static_cast<size_t>(out_features) * in_features) ||
+                     overlaps(y, yb, x_scales, static_cast<size_t>(n_rows) * 4) ||
+                     overlaps(y, yb, w_scales, static_cast<size_t>(out_features) * 4)))
+    return fail(SA_ERR_RANGE, "y overlaps an input");
+  sa::ProjArgs a{};
+  a.x = x_codes;
+  a.n_tok = n_rows;
+  a.hidden = in_features;
+  a.width = out_features;
+  a.n_seg = 1;
+  for (int i = 0; i < 3; ++i) {
+    a.seg[i] = sa::ProjSeg{w_codes, y, sa::kOutRows};
+    a.w_scale[i] = w_scales;
+  }
+  a.op = op;
+  a.x_scale = x_scales;
+  const hipError_t e = sa::launch_proj(a, sa::kBF16, device_cus(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return ok();
+}
+
+// Checks shared by the 8-bit cache projections (before any state is read).
+static sa_status check_cache_q8(const sa_cache* c, sa_qtype qtype, int* op, int32_t hidden) {
+  if (sa_status s = q8_op(qtype, op)) return s;
+  if (c->desc.dtype == SA_F32) return fail(SA_ERR_DTYPE, "8-bit projections write bf16 or e4m3 caches only");
+  return check_q8_hidden(hidden);
+}
+
+sa_status sa_cache_recache_q8(sa_cache* c, const void* x_codes, const float* x_scales, const void* wk_codes,
+                              const float* wk_scales, const void* wv_codes, const float* wv_scales, sa_qtype qtype,
+                              int32_t hidden, void* stream) {
+  if (!c || !x_codes || !x_scales || !wk_codes || !wk_scales || !wv_codes || !wv_scales)
+    return fail(SA_ERR_NULL, "cache, codes and scales must be non-NULL");
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(wk_codes) || !aligned16(wk_scales) ||
+      !aligned16(wv_codes) || !aligned16(wv_scales))
+    return fail(SA_ERR_ALIGN, "codes and scales must be 16-byte aligned");
+  int op = 0;
+  if (sa_status s = check_cache_q8(c, qtype, &op, hidden)) return s;
+  const int hd = c->desc.n_heads * c->desc.head_dim;
+  if (sa_status s = check_proj_sizes(0, hidden, hd, 1)) return s;
+  if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "recache on an empty cache");
+  const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * c->plan.resident().size() * c->desc.tokens_per_frame;
+  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, 1)) return s;
+  sa::ProjArgs a = cache_proj_args(c, x_codes, nullptr, nullptr, wk_codes, wv_codes, hidden);
+  a.w_scale[0] = wk_scales;
+  a.w_scale[1] = a.w_scale[2] = wv_scales;
+  a.op = op;
+  a.x_scale = x_scales;
+  a.n_tok = n_tok;
+  a.frames = resident_table(c);
+  const hipError_t e = sa::launch_proj(a, sa::kBF16, device_cus(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "recache launch");
+  return ok();
+}
+
+sa_status sa_cache_project_append_q8(sa_cache* c, const void* x_codes, const float* x_scales, const void* wq_codes,
+                                     const float* wq_scales, const void* wk_codes, const float* wk_scales,
+                                     const void* wv_codes, const float* wv_scales, sa_qtype qtype, int32_t hidden,
+                                     void* q_out, int32_t n_frames, int64_t t0, void* stream) {
+  if (!c || !x_codes || !x_scales || !wk_codes || !wk_scales || !wv_codes || !wv_scales)
+    return fail(SA_ERR_NULL, "cache, codes and scales must be non-NULL");
+  if (!wq_codes != !q_out || !wq_codes != !wq_scales)
+    return fail(SA_ERR_NULL, "wq_codes, wq_scales and q_out must all be given or all be NULL");
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(wk_codes) || !aligned16(wk_scales) ||
+      !aligned16(wv_codes) || !aligned16(wv_scales) || !aligned16(wq_codes) || !aligned16(wq_scales) ||
+      !aligned16(q_out))
+    return fail(SA_ERR_ALIGN, "codes, scales and q_out must be 16-byte aligned");
+  int op = 0;
+  if (sa_status s = check_cache_q8(c, qtype, &op, hidden)) return s;
+  if (t0 < 0 || t0 > (int64_t(1) << 40)) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40]");
+  if (sa_status s = check_append_chunk(c, n_frames, t0)) return s;
+  const int hd = c->desc.n_heads * c->desc.head_dim;
+  const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * n_frames * c->desc.tokens_per_frame;
+  if (sa_status s = check_proj_sizes(n_tok, hidden, hd, 1)) return s;
+  sa::ProjArgs a = cache_proj_args(c, x_codes, wq_codes, q_out, wk_codes, wv_codes, hidden);
+  int n = 0;
+  if (wq_codes) a.w_scale[n++] = wq_scales;
+  a.w_scale[n++] = wk_scales;
+  a.w_scale[n++] = wv_scales;
+  for (int i = n; i < 3; ++i) a.w_scale[i] = wv_scales;
+  a.op = op;
+  a.x_scale = x_scales;
+  a.n_tok = n_tok;
+  a.frames = chunk_table(c, n_frames, t0);
+  const hipError_t e = sa::launch_proj(a, sa::kBF16, device_cus(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  c->plan.commit_append(n_frames, t0);
+  return ok();
+}
+
 static sa_status attn_plan(const sa_cache* c, int32_t n_q, int* splits, size_t* bytes) {
   if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "attention on an empty cache");
   const auto res = c->plan.resident();

@@ -70,6 +70,10 @@ enum ProjOut : int {
   kOutCacheK = 1,  // rotated at the token's frame time, into the key store
   kOutCacheV = 2,  // into the transposed value store
 };
+// Operand types: bf16, or 8-bit codes (e4m3 / int8) with an fp32 scale per
+// x row (token) and per weight row (output feature):
+//   out[n][f] = (float(sum_c qx[n][c] qw[f][c]) * sx[n]) * sw[f].
+enum ProjOp : int { kOpBF16 = 0, kOpE4M3 = 1, kOpI8 = 2 };
 struct ProjSeg {
   const void* w;  // [width][C]
   void* y;        // kOutRows only
@@ -84,6 +88,9 @@ struct ProjArgs {
   ProjSeg seg[3];
   int32_t has_key, has_value;  // some segment is kOutCacheK / kOutCacheV
   int32_t cache_fp8;           // cache outputs go to an e4m3 cache (bf16-rounded results, scaled)
+  int32_t op;                  // ProjOp of x and the weights (the output is bf16 unless op and dtype are fp32)
+  const float* x_scale;        // [n_tok], 8-bit operands only
+  const float* w_scale[3];     // [width] per segment, 8-bit operands only (16-byte aligned)
   // Cache outputs only: token n is token tok of frame j of stream b, with
   // n = (b * frames.n + j) * T + tok.
   CacheGeom g;
@@ -112,5 +119,8 @@ hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream);
 // 0 = 256 x 128, 1 = 128 x 128, 2 = 128 x 64 (features x tokens).
 int proj_tile_shape(int64_t n_tok, int F, int num_cus);
 hipError_t launch_proj(const ProjArgs& a, int dtype, int num_cus, hipStream_t stream);
+// Row-wise 8-bit quantisation (op = kOpI8 or kOpE4M3) of x [n_rows][n_cols] bf16.
+hipError_t launch_quantize_rows(const void* x, void* codes, float* scales, int op, int64_t n_rows, int n_cols,
+                                hipStream_t stream);
 
 }  // namespace sa

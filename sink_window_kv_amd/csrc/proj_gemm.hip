@@ -15,6 +15,11 @@
 //     [slot][b][h][d][tok].
 // An e4m3 cache receives the bf16-rounded results divided by its scales and
 // rounded to e4m3 (8-byte pieces).
+// Operands are bf16, or 8-bit codes (int8 or OCP e4m3) with an fp32 scale per
+// token row of x and per weight row, for the 8-bit projections (LongLive
+// paper review, "INT8 quantized inference" table; model card FP8 variant):
+// the products run on v_mfma_i32_32x32x32_i8 / v_mfma_scale_f32_32x32x64_
+// f8f6f4 and the epilogue applies the two scales before everything else.
 // Three entry points use it:
 //   * KV recache at a prompt switch (LongLive paper review, section 3 "KV
 //     Recache"): segments (W_k -> key cache, W_v -> value cache) over every
@@ -30,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.hpp"
 
@@ -38,8 +44,12 @@ namespace {
 
 typedef __bf16 mfma_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float mfma_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTK = 32;     // reduction slice per LDS stage
+// A reduction slice is 64 bytes of every operand row: 32 bf16 or 64 8-bit codes.
+constexpr int kSliceBytes = 64;
 constexpr int kGWaves = 4;  // waves per workgroup, a 2 x 2 grid of wave tiles
 constexpr int kOPad = 8;    // epilogue tile row padding (bf16 elements)
 #ifndef PROJ_PRE
@@ -47,7 +57,7 @@ constexpr int kOPad = 8;    // epilogue tile row padding (bf16 elements)
 #endif
 constexpr int kPre = PROJ_PRE;  // reduction slices in flight in registers
 
-// LDS stage: rows of kTK bf16 = 4 chunks of 16 bytes, chunk (r, c) stored at
+// LDS stage: rows of one 64-byte slice = 4 chunks of 16 bytes, chunk (r, c) stored at
 // r*4 + (c ^ swz(r)).  A 16-byte LDS read is served 16 lanes at a time, and
 // the 16 lanes of an operand read take 16 consecutive rows at one chunk
 // index: 4 rows share each 256-byte line of the 64 banks, and the swizzle
@@ -97,8 +107,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, ui
 // multiplies the current one, with one barrier per step.  Plain vector loads
 // stage the slices (the direct-to-LDS path moves far fewer bytes per cycle
 // per CU).
-template <int TM, int TN>
-__global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) {
+template <int TM, int TN, int QT>
+__device__ __forceinline__ void proj_body(ProjArgs a) {
+  constexpr int EB = QT == kOpBF16 ? 2 : 1;    // operand bytes per element
+  constexpr int TKE = kSliceBytes / EB;        // reduction elements per slice
+  using Acc = typename std::conditional<QT == kOpI8, i32x16, mfma_f32x16>::type;
   constexpr int MI = TM / 64;                  // 32-row products per wave (features)
   constexpr int NJ = TN / 64;                  // 32-column products per wave (tokens)
   constexpr int kAI = TM * 4 / (kGWaves * 64); // feature-tile transfers per wave per slice
@@ -117,11 +130,11 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
   const int64_t n_tok = a.n_tok;
   const int m0 = blockIdx.y * TM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * TN;
-  const uint64_t w_bytes = static_cast<uint64_t>(width) * C * 2;
+  const uint64_t w_bytes = static_cast<uint64_t>(width) * C * EB;
   const __amdgpu_buffer_rsrc_t w0 = gemm_rsrc(a.seg[0].w, w_bytes);
   const __amdgpu_buffer_rsrc_t w1 = gemm_rsrc(a.seg[1].w, w_bytes);
   const __amdgpu_buffer_rsrc_t w2 = gemm_rsrc(a.seg[2].w, w_bytes);
-  const __amdgpu_buffer_rsrc_t xr = gemm_rsrc(a.x, static_cast<uint64_t>(n_tok) * C * 2);
+  const __amdgpu_buffer_rsrc_t xr = gemm_rsrc(a.x, static_cast<uint64_t>(n_tok) * C * EB);
 
   // Per-lane source offsets (bytes, at reduction offset 0) of this wave's
   // transfers into the feature and token tiles.  A transfer covers 16 rows,
@@ -138,7 +151,7 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
     s = s < a.n_seg ? s : a.n_seg - 1;
     arsrc[u] = s == 0 ? w0 : (s == 1 ? w1 : w2);
     const int fl = m0 + r - s * width;
-    aoff[u] = static_cast<uint32_t>((static_cast<uint64_t>(fl) * C + c * 8) * 2);
+    aoff[u] = static_cast<uint32_t>(static_cast<uint64_t>(fl) * C * EB + c * 16);
   }
 #pragma unroll
   for (int u = 0; u < kBI; ++u) {
@@ -146,7 +159,7 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
     const int r = P >> 2, c = (P & 3) ^ gswz(r);
     const uint64_t tkn = static_cast<uint64_t>(n0 + r);
     // tokens past the end read past the buffer: zero
-    const uint64_t off = (tkn * C + c * 8) * 2;
+    const uint64_t off = tkn * C * EB + c * 16;
     boff[u] = off >= 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(off);
   }
 
@@ -157,30 +170,30 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
 #pragma unroll
   for (int j = 0; j < NJ; ++j) brow[j] = wn * (TN / 2) + 32 * j + n;
 
-  mfma_f32x16 acc[MI][NJ];
+  Acc acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   // Slices go global -> registers -> LDS through kPre register buffers:
   // step ks writes slice ks+1 (loaded kPre steps earlier) into the LDS stage
   // that slice ks-1 was read from, reloads that register buffer with slice
   // ks+1+kPre and multiplies slice ks.  The step loop is unrolled by kPre so
   // that every register buffer index is static.
-  const int nk = C / kTK;
+  const int nk = C / TKE;
   u32x4 R[kPre][kAI + kBI];
   auto load_regs = [&](u32x4 (&Rb)[kAI + kBI], int k0) {
 #pragma unroll
     for (int u = 0; u < kAI; ++u)
       Rb[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                  arsrc[u], static_cast<int>(aoff[u] + k0 * 2), 0, 0));
+                  arsrc[u], static_cast<int>(aoff[u] + k0 * EB), 0, 0));
 #pragma unroll
     for (int u = 0; u < kBI; ++u)
       Rb[kAI + u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        xr, static_cast<int>(boff[u] == 0xffffffffu ? boff[u] : boff[u] + k0 * 2), 0, 0));
+                        xr, static_cast<int>(boff[u] == 0xffffffffu ? boff[u] : boff[u] + k0 * EB), 0, 0));
   };
   auto store_regs = [&](const u32x4 (&Rb)[kAI + kBI], GemmStage<TM, TN>& st) {
 #pragma unroll
@@ -193,26 +206,56 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
   // are never multiplied), so inside the loop the compiler's load-completion
   // waits stay exact: each step waits only for the slice it stores, not for
   // the kPre - 1 slices loaded after it.
-  const int last = (nk - 1) * kTK;
+  const int last = (nk - 1) * TKE;
   load_regs(R[0], 0);
   store_regs(R[0], stg[0]);
 #pragma unroll
-  for (int p = 1; p <= kPre; ++p) load_regs(R[p % kPre], min(p * kTK, last));
+  for (int p = 1; p <= kPre; ++p) load_regs(R[p % kPre], min(p * TKE, last));
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // The reduction index of an operand byte only has to be the same for both
+  // operands: lane half hh takes chunk 2s + hh of the slice in step s (bf16,
+  // int8: 16 bytes per lane per product), or chunks 2hh and 2hh + 1 (e4m3:
+  // 32 bytes per lane, one product per slice).
   auto multiply = [&](const GemmStage<TM, TN>& st) {
+    if constexpr (QT == kOpE4M3) {
+      i32x8 af[MI], bfr[NJ];
 #pragma unroll
-    for (int s = 0; s < kTK / 16; ++s) {
-      mfma_bf16x8 af[MI], bfr[NJ];
-      const int kc = 2 * s + hh;
+      for (int i = 0; i < MI; ++i) {
+        const u32x4 lo = st.a[arow[i] * 4 + ((2 * hh) ^ gswz(arow[i]))];
+        const u32x4 hi = st.a[arow[i] * 4 + ((2 * hh + 1) ^ gswz(arow[i]))];
+        af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
 #pragma unroll
-      for (int i = 0; i < MI; ++i) af[i] = as_bf16x8(st.a[arow[i] * 4 + (kc ^ gswz(arow[i]))]);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[j] = as_bf16x8(st.b[brow[j] * 4 + (kc ^ gswz(brow[j]))]);
+      for (int j = 0; j < NJ; ++j) {
+        const u32x4 lo = st.b[brow[j] * 4 + ((2 * hh) ^ gswz(brow[j]))];
+        const u32x4 hi = st.b[brow[j] * 4 + ((2 * hh + 1) ^ gswz(brow[j]))];
+        bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 af[MI], bfr[NJ];
+        const int kc = 2 * s + hh;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[i] = st.a[arow[i] * 4 + (kc ^ gswz(arow[i]))];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bfr[j] = st.b[brow[j] * 4 + (kc ^ gswz(brow[j]))];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            if constexpr (QT == kOpI8)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, af[i]),
+                                                                 __builtin_bit_cast(i32x4, bfr[j]), acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j], 0, 0, 0);
+          }
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
@@ -226,7 +269,7 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
     for (int p = 0; p < kPre; ++p) {
       const int ks = kb + p;
       store_regs(R[(p + 1) % kPre], stg[(ks + 1) & 1]);
-      load_regs(R[(p + 1) % kPre], min((ks + 1 + kPre) * kTK, last));
+      load_regs(R[(p + 1) % kPre], min((ks + 1 + kPre) * TKE, last));
       multiply(stg[ks & 1]);
     }
   }
@@ -256,13 +299,26 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
     int b = 0, lf = 0, tok = 0;
     if (a.has_key && tkn < n_tok) token_coords(tkn, per_stream, g.T, &b, &lf, &tok);
     const int64_t t = a.has_key ? a.frames.t[lf] : 0;
+    float sx = 1.f;
+    if constexpr (QT != kOpBF16) sx = tkn < n_tok ? a.x_scale[tkn] : 0.f;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int fl = wm * (TM / 2) + 32 * i + 8 * q + 4 * hh;
         const int f = m0 + fl;  // multiple of 4
-        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        float v[4] = {static_cast<float>(acc[i][j][4 * q]), static_cast<float>(acc[i][j][4 * q + 1]),
+                      static_cast<float>(acc[i][j][4 * q + 2]), static_cast<float>(acc[i][j][4 * q + 3])};
+        if constexpr (QT != kOpBF16) {
+          // (acc * sx[token]) * sw[feature]; the 4 features lie in one segment
+          f32x4 sw = {0.f, 0.f, 0.f, 0.f};
+          if (f < F) {
+            const int s = f / width;
+            sw = *reinterpret_cast<const f32x4*>(a.w_scale[s] + (f - s * width));
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (v[r] * sx) * sw[r];
+        }
         if (a.has_key && f < F) {
           const int s = f / width;
           if (a.seg[s].kind == kOutCacheK) {
@@ -344,6 +400,17 @@ __global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) 
   }
 }
 
+template <int TM, int TN>
+__global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) {
+  proj_body<TM, TN, kOpBF16>(a);
+}
+
+// 8-bit operands (QT = kOpE4M3 or kOpI8), bf16 results.
+template <int TM, int TN, int QT>
+__global__ void __launch_bounds__(kGWaves * 64, 2) proj_q8_kernel(ProjArgs a) {
+  proj_body<TM, TN, QT>(a);
+}
+
 // fp32 path (small configurations): one thread per (token, 4 output features).
 __global__ void __launch_bounds__(256) proj_f32_kernel(ProjArgs a) {
   const CacheGeom& g = a.g;
@@ -407,7 +474,12 @@ template <int TM, int TN>
 void launch_tile(const ProjArgs& a, hipStream_t stream) {
   const int F = a.n_seg * a.width;
   const dim3 grid(static_cast<unsigned>((a.n_tok + TN - 1) / TN), static_cast<unsigned>((F + TM - 1) / TM));
-  hipLaunchKernelGGL((proj_bf16_kernel<TM, TN>), grid, dim3(kGWaves * 64), 0, stream, a);
+  if (a.op == kOpE4M3)
+    hipLaunchKernelGGL((proj_q8_kernel<TM, TN, kOpE4M3>), grid, dim3(kGWaves * 64), 0, stream, a);
+  else if (a.op == kOpI8)
+    hipLaunchKernelGGL((proj_q8_kernel<TM, TN, kOpI8>), grid, dim3(kGWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((proj_bf16_kernel<TM, TN>), grid, dim3(kGWaves * 64), 0, stream, a);
 }
 
 int64_t tiles_of(int64_t n_tok, int F, int TM, int TN) { return ((n_tok + TN - 1) / TN) * ((F + TM - 1) / TM); }

@@ -161,6 +161,31 @@ def test_cache_plan_rejections_and_reset(plan_harness):
     assert rows[4][1] == 12 and rows[5][1] == 0 and rows[6][2] == [(0, 0, 0, 0)]
 
 
+def test_host_q8_validation():
+    """Argument checks of the 8-bit entry points that fail before any launch (no call reaches the GPU)."""
+    swk = _swk()
+    L = swk.lib()
+    P, Q, R, S1, S2 = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    I8, E4 = swk.SA_Q_INT8, swk.SA_Q_E4M3
+    assert L.sa_quantize_rows(None, Q, S1, I8, 4, 64, None) == swk.SA_ERR_NULL
+    assert L.sa_quantize_rows(P, Q, S1, 5, 4, 64, None) == swk.SA_ERR_DTYPE
+    assert L.sa_quantize_rows(P, Q + 4, S1, I8, 4, 64, None) == swk.SA_ERR_ALIGN
+    assert L.sa_quantize_rows(P, Q, S1, E4, 4, 60, None) == swk.SA_ERR_SHAPE      # cols % 8
+    assert L.sa_quantize_rows(P, Q, S1, E4, -1, 64, None) == swk.SA_ERR_SHAPE
+    assert L.sa_quantize_rows(P, Q, S1, I8, 0, 64, None) == swk.SA_OK             # nothing to do
+    assert L.sa_linear_q8(P, S1, Q, S2, None, I8, 4, 64, 64, None) == swk.SA_ERR_NULL
+    assert L.sa_linear_q8(P, S1, Q, S2, R, 9, 4, 64, 64, None) == swk.SA_ERR_DTYPE
+    assert L.sa_linear_q8(P, S1 + 4, Q, S2, R, I8, 4, 64, 64, None) == swk.SA_ERR_ALIGN
+    assert L.sa_linear_q8(P, S1, Q, S2, R, I8, 4, 96, 64, None) == swk.SA_ERR_SHAPE   # in % 64
+    assert L.sa_linear_q8(P, S1, Q, S2, R, E4, 4, 64, 40, None) == swk.SA_ERR_SHAPE   # out % 16
+    assert L.sa_linear_q8(P, S1, Q, S2, P + 64, I8, 4, 64, 64, None) == swk.SA_ERR_RANGE  # y overlaps x
+    assert L.sa_linear_q8(P, S1, Q, S2, S2, E4, 4, 64, 64, None) == swk.SA_ERR_RANGE      # y overlaps w_scales
+    assert L.sa_linear_q8(P, S1, Q, S2, R, E4, 0, 64, 64, None) == swk.SA_OK
+    assert L.sa_cache_recache_q8(None, P, S1, Q, S2, R, S2, I8, 64, None) == swk.SA_ERR_NULL
+    assert L.sa_cache_project_append_q8(None, P, S1, None, None, Q, S2, R, S2, I8, 64, None, 1, 0, None) == \
+        swk.SA_ERR_NULL
+
+
 def test_host_projection_validation():
     """Argument checks of sa_linear / sa_cache_project_append that fail before any launch."""
     L = _swk().lib()
