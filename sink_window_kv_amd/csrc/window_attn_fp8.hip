@@ -285,9 +285,33 @@ __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
                                        __builtin_amdgcn_exp2f(sacc[kb][i0 + 2]), __builtin_amdgcn_exp2f(sacc[kb][i0 + 3])));
     }
     lacc = mfma_f8(ones, pk, lacc, 127);
+    // The frame's tail tile: its V^T bytes past the frame end come from
+    // whatever follows the row in memory (for the last channel, the next
+    // (slot, stream, head) block, possibly never written, possibly NaN codes).
+    // Their p is 0, but 0 * NaN is NaN, so those bytes are cleared first:
+    // lane half hh holds keys jl0 + 32hh + 4w .. +3 in dword w of the operand.
+    uint32_t vmask[8];
+    const bool vtail = jl0 + kKTile > T;  // wave-uniform
+    if (vtail) {
+      const int kk = T - jl0 - 32 * hh;  // valid keys among this lane's 32
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      oacc[db] = mfma_f8(as_v8i(rd(st, vaddr[0] + db * 2048), rd(st, vaddr[1] + db * 2048)), pk, oacc[db], 127);
+      for (int w = 0; w < 8; ++w) {
+        const int nb = min(max(kk - 4 * w, 0), 4);
+        vmask[w] = nb == 4 ? 0xffffffffu : ((1u << (8 * nb)) - 1u);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      u32x4 lo = rd(st, vaddr[0] + db * 2048), hi = rd(st, vaddr[1] + db * 2048);
+      if (vtail) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          lo[w] &= vmask[w];
+          hi[w] &= vmask[4 + w];
+        }
+      }
+      oacc[db] = mfma_f8(as_v8i(lo, hi), pk, oacc[db], 127);
+    }
   };
 
   // three stages, two tiles in flight (as the bf16 eight-wave path)

@@ -174,6 +174,32 @@ def test_position_interpolation_f32_fractional():
         _check(gs, q, o, True, what=f"PI 1/3 f32 frame {f}")
 
 
+@pytest.mark.parametrize("grid", [(4, 10), (30, 52)])
+def test_stores_start_as_nan_bits(grid):
+    """Every bf16 of both stores starts as 0xffff (NaN) and ring slots fill one frame at a time: no unwritten
+    slot and no byte past a frame's keys may reach the output (both masks, both workgroup shapes)."""
+    import dataclasses
+    import torch
+    swk = _swk()
+    w = dataclasses.replace(wl.WORKLOADS[2], name="bf16-nan-fill", cfg=55, n_heads=4 if grid == (4, 10) else 12,
+                            grid=grid, frames=6, batch=2 if grid == (4, 10) else 1)
+    rows = None if grid == (4, 10) else sample_rows(w.tokens_per_frame, w.tokens_per_frame, n=48, seed=6)
+    for waves in ("8", "4"):
+        gs = GpuStream(w)
+        gs.cache.k_store.view(torch.int16).fill_(-1)   # bf16 bits 0xffff: a NaN
+        gs.cache.v_store.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        with _env(SA_ATTN_WAVES=waves):
+            for f in range(w.frames):
+                q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+                gs.append(k, v, 1, f)
+                for mask in (swk.SA_MASK_FRAME_CAUSAL, swk.SA_MASK_NONE):
+                    o = gs.attend(q, 1, mask)
+                    assert torch.isfinite(o).all(), f"frame {f} mask {mask} waves {waves}"
+                    _check(gs, q, o, mask == swk.SA_MASK_FRAME_CAUSAL, rows=rows,
+                           what=f"nan-filled stores frame {f} mask {mask} waves {waves}")
+
+
 def test_cfg2_unscaled_scores_and_custom_scale():
     """Second draw: unscaled N(0,1) Q and K (score std ~ 1) and a non-default scale (score std ~ 0.6).
 

@@ -142,6 +142,29 @@ def test_fp8_attention_small(chunks, mask):
         f0 += c
 
 
+@pytest.mark.parametrize("grid", [(4, 10), (30, 52)])
+def test_fp8_attention_stores_start_as_nan_codes(grid):
+    """Regression: every byte of both e4m3 stores starts as 0xff (a NaN code) and ring slots fill one frame at a
+    time, so the bytes that follow a frame's last key (tail tiles: T = 40 and 1560 are not multiples of 64) and
+    the not-yet-written slots hold NaN codes; the attention must read none of them into its output."""
+    import dataclasses
+    import torch
+    swk = _swk()
+    w = dataclasses.replace(wl.WORKLOADS[2], name="fp8-nan-fill", cfg=54, n_heads=4 if grid == (4, 10) else 12,
+                            grid=grid, frames=6, batch=2 if grid == (4, 10) else 1)
+    gs = Fp8Stream(w, k_scale=1.0 / 64, v_scale=1.0 / 64)
+    gs.cache.k_store.fill_(0xFF)
+    gs.cache.v_store.fill_(0xFF)
+    torch.cuda.synchronize()
+    rows = None if grid == (4, 10) else sample_rows(w.tokens_per_frame, w.tokens_per_frame, n=48, seed=4)
+    for f in range(w.frames):
+        q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+        gs.append(k, v, 1, f)
+        for mask in (swk.SA_MASK_FRAME_CAUSAL, swk.SA_MASK_NONE):
+            o = gs.attend(q, 1, mask)
+            _check_fp8(gs, q, o, mask == swk.SA_MASK_FRAME_CAUSAL, rows=rows, what=f"nan-filled stores frame {f} mask {mask}")
+
+
 @pytest.mark.parametrize("splits", [None, "1", "5"])
 def test_fp8_attention_wan_layer(splits):
     """Wan-1.3B layer in an e4m3 cache: 3 sink + 9 local frames of 1560 tokens (24 full tiles and one of
