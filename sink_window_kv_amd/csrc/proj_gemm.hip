@@ -207,6 +207,40 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
   // waits stay exact: each step waits only for the slice it stores, not for
   // the kPre - 1 slices loaded after it.
   const int last = (nk - 1) * TKE;
+  // Per-token coordinates of the tile for the cache outputs, computed once
+  // here (one division per token) instead of per output piece: frame time,
+  // grid row and column, and the element offsets of the token's key row and
+  // value column at head 0, channel 0.
+  const CacheGeom& g = a.g;
+  const int dshift = g.D == 128 ? 7 : 6;  // head_dim is 64 or 128
+  __shared__ int s_row[TN], s_col[TN];
+  __shared__ int64_t s_t[TN], s_kb[TN], s_vb[TN];
+  if (a.has_key || a.has_value) {
+    const int per_stream = a.frames.n * g.T;
+    for (int t = threadIdx.x; t < TN; t += kGWaves * 64) {
+      const int64_t tkn = n0 + t;
+      int row = 0, col = 0;
+      int64_t tt = 0, kb = 0, vb = 0;
+      if (tkn < n_tok) {
+        const int nn = static_cast<int>(tkn);  // < 2^31: x is below 4 GiB
+        const int b = nn / per_stream;
+        const int rem = nn - b * per_stream;
+        const int lf = rem / g.T;
+        const int tok = rem - lf * g.T;
+        row = tok / a.rope.grid_w;
+        col = tok - row * a.rope.grid_w;
+        tt = a.frames.t[lf];
+        const int64_t sb = (static_cast<int64_t>(a.frames.store_slot[lf]) * g.B + b) * g.H;  // (slot, b, head 0)
+        kb = (sb * g.T + tok) * g.D;
+        vb = sb * g.D * g.T + tok;
+      }
+      s_row[t] = row;
+      s_col[t] = col;
+      s_t[t] = tt;
+      s_kb[t] = kb;
+      s_vb[t] = vb;
+    }
+  }
   load_regs(R[0], 0);
   store_regs(R[0], stg[0]);
 #pragma unroll
@@ -289,16 +323,20 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
   // rounded to bf16 into the LDS tile, then written out in 16-byte pieces:
   // row-major and key rows [tok][d] directly, value rows [d][tok] gathered
   // per feature.
-  const CacheGeom& g = a.g;
-  const int per_stream = a.frames.n * g.T;
+  // The segment of feature f: at most three, so two compares.
+  auto seg_of = [&](int f) { return (f >= width ? 1 : 0) + (f >= 2 * width ? 1 : 0); };
   asm volatile("s_barrier" ::: "memory");  // every wave is done with the stages
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int tl = wn * (TN / 2) + 32 * j + n;
     const int64_t tkn = n0 + tl;
-    int b = 0, lf = 0, tok = 0;
-    if (a.has_key && tkn < n_tok) token_coords(tkn, per_stream, g.T, &b, &lf, &tok);
-    const int64_t t = a.has_key ? a.frames.t[lf] : 0;
+    int row = 0, col = 0;
+    int64_t t = 0;
+    if (a.has_key) {
+      row = s_row[tl];
+      col = s_col[tl];
+      t = s_t[tl];
+    }
     float sx = 1.f;
     if constexpr (QT != kOpBF16) sx = tkn < n_tok ? a.x_scale[tkn] : 0.f;
 #pragma unroll
@@ -313,22 +351,22 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
           // (acc * sx[token]) * sw[feature]; the 4 features lie in one segment
           f32x4 sw = {0.f, 0.f, 0.f, 0.f};
           if (f < F) {
-            const int s = f / width;
+            const int s = seg_of(f);
             sw = *reinterpret_cast<const f32x4*>(a.w_scale[s] + (f - s * width));
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = (v[r] * sx) * sw[r];
         }
         if (a.has_key && f < F) {
-          const int s = f / width;
+          const int s = seg_of(f);
           if (a.seg[s].kind == kOutCacheK) {
             const int fs = f - s * width;
-            const int head = fs / g.D, d = fs - head * g.D;
+            const int head = fs >> dshift, d = fs & (g.D - 1);
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
               const int p = d / 2 + pp;
               float sn, cs;
-              rope_cs(a.rope, head, p, t, tok / a.rope.grid_w, tok % a.rope.grid_w, &sn, &cs);
+              rope_cs(a.rope, head, p, t, row, col, &sn, &cs);
               const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
               v[2 * pp] = x0 * cs - x1 * sn;
               v[2 * pp + 1] = x0 * sn + x1 * cs;
@@ -350,17 +388,14 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
     const int64_t tkn = n0 + tl;
     const int f = m0 + fl;
     if (tkn >= n_tok || f >= F) continue;
-    const int s = f / width;
+    const int s = seg_of(f);
     const int fs = f - s * width;
     const u32x4 piece = *reinterpret_cast<const u32x4*>(&sm.out.o[tl][fl]);
     if (a.seg[s].kind == kOutRows) {
       *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.seg[s].y) + tkn * width + fs) = piece;
     } else if (a.seg[s].kind == kOutCacheK) {
-      int b, lf, tok;
-      token_coords(tkn, per_stream, g.T, &b, &lf, &tok);
-      const int64_t slot = a.frames.store_slot[lf];
-      const int head = fs / g.D, d = fs - head * g.D;
-      const int64_t idx = (((slot * g.B + b) * g.H + head) * g.T + tok) * g.D + d;
+      const int head = fs >> dshift, d = fs & (g.D - 1);
+      const int64_t idx = s_kb[tl] + static_cast<int64_t>(head) * g.T * g.D + d;
       if (a.cache_fp8) {
         float x[8];
         unpack_bf16x8(piece, x);
@@ -377,18 +412,15 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
     const int f = m0 + fl;
     const int64_t tkn0 = n0 + tl;
     if (f >= F || tkn0 >= n_tok) continue;
-    const int s = f / width;
+    const int s = seg_of(f);
     if (a.seg[s].kind != kOutCacheV) continue;
     // 8 consecutive tokens stay in one frame and stream (T % 8 == 0)
-    int b, lf, tok;
-    token_coords(tkn0, per_stream, g.T, &b, &lf, &tok);
-    const int64_t slot = a.frames.store_slot[lf];
     const int fv = f - s * width;
-    const int head = fv / g.D, d = fv - head * g.D;
+    const int head = fv >> dshift, d = fv & (g.D - 1);
     uint16_t vals[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) vals[r] = sm.out.o[tl + r][fl];
-    const int64_t idx = (((slot * g.B + b) * g.H + head) * g.D + d) * g.T + tok;
+    const int64_t idx = s_vb[tl] + static_cast<int64_t>(head * g.D + d) * g.T;
     if (a.cache_fp8) {
       float x[8];
 #pragma unroll
