@@ -70,10 +70,13 @@ struct GemmStage {
 };
 __device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 // Epilogue tile: the workgroup's results in bf16, [token][feature] (padded
-// rows), so that every output layout is written in whole 16-byte pieces.
+// rows), so that every output layout is written in whole 16-byte pieces; a
+// tile made only of value features is kept [feature][token] instead, the
+// order of the transposed value store.
 template <int TM, int TN>
-struct GemmOut {
+union GemmOut {
   uint16_t o[TN][TM + kOPad];
+  uint16_t ot[TM][TN + kOPad];
 };
 template <int TM, int TN>
 union GemmSmem {
@@ -325,6 +328,10 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
   // per feature.
   // The segment of feature f: at most three, so two compares.
   auto seg_of = [&](int f) { return (f >= width ? 1 : 0) + (f >= 2 * width ? 1 : 0); };
+  // A tile of value features only (the recache and per-frame projections put
+  // the value segment last and tiles are aligned to it when the width is a
+  // multiple of the tile): kept transposed in LDS.
+  const bool allv = a.has_value && m0 >= (a.n_seg - 1) * width && a.seg[a.n_seg - 1].kind == kOutCacheV;
   asm volatile("s_barrier" ::: "memory");  // every wave is done with the stages
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -373,17 +380,22 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
             }
           }
         }
-        uint2 w;
-        w.x = pack_bf16x2(v[0], v[1]);
-        w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(&sm.out.o[tl][fl]) = w;
+        if (allv) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.out.ot[fl + r][tl] = static_cast<uint16_t>(f32_to_bf16_bits(v[r]));
+        } else {
+          uint2 w;
+          w.x = pack_bf16x2(v[0], v[1]);
+          w.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(&sm.out.o[tl][fl]) = w;
+        }
       }
   }
   __syncthreads();
   uint16_t* kst = static_cast<uint16_t*>(g.k_store);
   uint16_t* vst = static_cast<uint16_t*>(g.v_store);
   // 16-byte pieces (token, 8 features): row-major outputs and keys
-  for (int e = threadIdx.x; e < TN * (TM / 8); e += kGWaves * 64) {
+  for (int e = allv ? TN * (TM / 8) : threadIdx.x; e < TN * (TM / 8); e += kGWaves * 64) {
     const int tl = e / (TM / 8), fl = (e % (TM / 8)) * 8;
     const int64_t tkn = n0 + tl;
     const int f = m0 + fl;
@@ -417,9 +429,13 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
     // 8 consecutive tokens stay in one frame and stream (T % 8 == 0)
     const int fv = f - s * width;
     const int head = fv >> dshift, d = fv & (g.D - 1);
-    uint16_t vals[8];
+    alignas(16) uint16_t vals[8];
+    if (allv) {
+      *reinterpret_cast<u32x4*>(vals) = *reinterpret_cast<const u32x4*>(&sm.out.ot[fl][tl]);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) vals[r] = sm.out.o[tl + r][fl];
+      for (int r = 0; r < 8; ++r) vals[r] = sm.out.o[tl + r][fl];
+    }
     const int64_t idx = s_vb[tl] + static_cast<int64_t>(head * g.D + d) * g.T;
     if (a.cache_fp8) {
       float x[8];
