@@ -244,6 +244,42 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
       s_vb[t] = vb;
     }
   }
+  // Time-axis cos / sin of the tile's key features.  With T >= TN the tile's
+  // tokens carry at most two frame times (its first and last token's), so
+  // each (time, head, time pair) is evaluated once here, by the same function
+  // as everywhere else, instead of once per output pair.
+  constexpr int kTcs = 384;  // 2 times x (TM / D + 1) heads x D / 2 pairs, TM <= 256
+  __shared__ float2 s_tcs[kTcs];
+  int tcs_h0 = 0, tcs_nh = 0;
+  int64_t tcs_t0 = 0;
+  if (a.has_key && g.T >= TN && a.rope.pairs_t > 0) {
+    int sk = -1;
+    for (int i = 0; i < a.n_seg; ++i)
+      if (a.seg[i].kind == kOutCacheK) sk = i;
+    const int kf0 = max(m0, sk * width), kf1 = min(m0 + TM, min(F, (sk + 1) * width));
+    if (sk >= 0 && kf0 < kf1) {
+      tcs_h0 = (kf0 - sk * width) >> dshift;
+      tcs_nh = ((kf1 - 1 - sk * width) >> dshift) - tcs_h0 + 1;
+      if (2 * tcs_nh * a.rope.pairs_t > kTcs) tcs_nh = 0;  // not for these shapes; kept as a guard
+      const int per_stream = a.frames.n * g.T;
+      auto time_of = [&](int64_t tkn) {
+        const int nn = static_cast<int>(tkn);
+        const int b = nn / per_stream;
+        return a.frames.t[(nn - b * per_stream) / g.T];
+      };
+      tcs_t0 = time_of(n0);
+      const int64_t t1 = time_of(min(n0 + TN, n_tok) - 1);
+      const int pt = a.rope.pairs_t;
+      for (int i = threadIdx.x; i < 2 * tcs_nh * pt; i += kGWaves * 64) {
+        const int fi = i / (tcs_nh * pt), rem = i - fi * tcs_nh * pt;
+        const int hh2 = rem / pt, pp = rem - hh2 * pt;
+        float sn, cs;
+        rope_sincos(static_cast<double>(fi ? t1 : tcs_t0),
+                    a.rope.freq[static_cast<size_t>(tcs_h0 + hh2) * a.rope.pairs_all + pp], &sn, &cs);
+        s_tcs[i] = float2{cs, sn};
+      }
+    }
+  }
   load_regs(R[0], 0);
   store_regs(R[0], stg[0]);
 #pragma unroll
@@ -373,7 +409,13 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
             for (int pp = 0; pp < 2; ++pp) {
               const int p = d / 2 + pp;
               float sn, cs;
-              rope_cs(a.rope, head, p, t, row, col, &sn, &cs);
+              if (tcs_nh > 0 && p < a.rope.pairs_t) {
+                const float2 e = s_tcs[((t == tcs_t0 ? 0 : 1) * tcs_nh + (head - tcs_h0)) * a.rope.pairs_t + p];
+                cs = e.x;
+                sn = e.y;
+              } else {
+                rope_cs(a.rope, head, p, t, row, col, &sn, &cs);
+              }
               const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
               v[2 * pp] = x0 * cs - x1 * sn;
               v[2 * pp + 1] = x0 * sn + x1 * cs;
