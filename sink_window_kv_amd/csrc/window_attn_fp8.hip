@@ -183,9 +183,16 @@ __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) vaddr[c] = kVtOff8 + static_cast<uint32_t>((n * 4 + ((2 * hh + c) ^ vswz8(n))) * 16);
 
-  // ---- global -> LDS: one K and one V^T transfer per wave per tile.
-  const u32x4 krsrc = buffer_rsrc(g.k_store, a.store_bytes);
-  const u32x4 vrsrc = buffer_rsrc(g.v_store, a.store_bytes);
+  // ---- global -> LDS: one K and one V^T transfer per wave per tile.  Each
+  // goes through a descriptor that covers just the frame's (slot, stream,
+  // head) block: the tail tile of a frame reads past the frame's keys, and
+  // past the block those bytes may be anything (a slot never written, NaN
+  // codes); the range check returns zeros for every dword beyond the block
+  // instead (dword by dword, so a piece that straddles the end keeps its
+  // valid part).  Beyond-frame keys are masked; their V^T bytes are then
+  // finite, so p = 0 contributes nothing.
+  const uint8_t* kst8 = static_cast<const uint8_t*>(g.k_store);
+  const uint8_t* vst8 = static_cast<const uint8_t*>(g.v_store);
   const int64_t head_off = static_cast<int64_t>(b) * g.H + h;
   const int64_t slot_stride = static_cast<int64_t>(g.B) * g.H;
   const uint32_t blk_bytes = static_cast<uint32_t>(T) * D;
@@ -201,6 +208,7 @@ __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
   // tiles are planned in non-decreasing order: frame of the tile tracked
   int pl_lf = 0, pl_end = ntf;
   struct Plan8 {
+    u32x4 krs, vrs;  // descriptors of the frame's K and V^T blocks
     uint32_t koff, voff;
   };
   auto plan = [&](int kt) {
@@ -212,15 +220,17 @@ __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
     const int slot = __builtin_amdgcn_readfirstlane(s_slot[min(pl_lf, n_res - 1)]);
     const uint32_t base = static_cast<uint32_t>((static_cast<int64_t>(slot) * slot_stride + head_off) * blk_bytes);
     Plan8 p;
-    p.koff = base + static_cast<uint32_t>(jl0) * D + klane;
-    p.voff = base + static_cast<uint32_t>(jl0) + vlane;
+    p.krs = buffer_rsrc(kst8 + base, blk_bytes);
+    p.vrs = buffer_rsrc(vst8 + base, blk_bytes);
+    p.koff = static_cast<uint32_t>(jl0) * D + klane;
+    p.voff = static_cast<uint32_t>(jl0) + vlane;
     return p;
   };
   auto fire = [&](const Plan8& p, int u, StageF8& st) {
     if (u == 0)
-      dma16(krsrc, p.koff, &st.k[64 * wave_u]);
+      dma16(p.krs, p.koff, &st.k[64 * wave_u]);
     else
-      dma16(vrsrc, p.voff, &st.vt[64 * wave_u]);
+      dma16(p.vrs, p.voff, &st.vt[64 * wave_u]);
   };
   auto issue = [&](int kt, StageF8& st) {
     const Plan8 p = plan(kt);
@@ -285,33 +295,9 @@ __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
                                        __builtin_amdgcn_exp2f(sacc[kb][i0 + 2]), __builtin_amdgcn_exp2f(sacc[kb][i0 + 3])));
     }
     lacc = mfma_f8(ones, pk, lacc, 127);
-    // The frame's tail tile: its V^T bytes past the frame end come from
-    // whatever follows the row in memory (for the last channel, the next
-    // (slot, stream, head) block, possibly never written, possibly NaN codes).
-    // Their p is 0, but 0 * NaN is NaN, so those bytes are cleared first:
-    // lane half hh holds keys jl0 + 32hh + 4w .. +3 in dword w of the operand.
-    uint32_t vmask[8];
-    const bool vtail = jl0 + kKTile > T;  // wave-uniform
-    if (vtail) {
-      const int kk = T - jl0 - 32 * hh;  // valid keys among this lane's 32
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int nb = min(max(kk - 4 * w, 0), 4);
-        vmask[w] = nb == 4 ? 0xffffffffu : ((1u << (8 * nb)) - 1u);
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      u32x4 lo = rd(st, vaddr[0] + db * 2048), hi = rd(st, vaddr[1] + db * 2048);
-      if (vtail) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          lo[w] &= vmask[w];
-          hi[w] &= vmask[4 + w];
-        }
-      }
-      oacc[db] = mfma_f8(as_v8i(lo, hi), pk, oacc[db], 127);
-    }
+    for (int db = 0; db < D / 32; ++db)
+      oacc[db] = mfma_f8(as_v8i(rd(st, vaddr[0] + db * 2048), rd(st, vaddr[1] + db * 2048)), pk, oacc[db], 127);
   };
 
   // three stages, two tiles in flight (as the bf16 eight-wave path)

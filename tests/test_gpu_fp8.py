@@ -165,6 +165,37 @@ def test_fp8_attention_stores_start_as_nan_codes(grid):
             _check_fp8(gs, q, o, mask == swk.SA_MASK_FRAME_CAUSAL, rows=rows, what=f"nan-filled stores frame {f} mask {mask}")
 
 
+@pytest.mark.parametrize("grid", [(4, 10), (30, 52)])
+def test_fp8_last_keys_of_the_last_channel(grid):
+    """T = 40 and 1560 leave 8 keys of a frame in a 16-key piece that straddles the frame's end; for the last
+    channel that piece straddles the (slot, stream, head) block.  V is 1 on exactly those keys of channel 127
+    and 0 elsewhere, q = 0 (uniform softmax): output channel 127 must be 8 / T in every row, the rest 0."""
+    import dataclasses
+    import torch
+    swk = _swk()
+    w = dataclasses.replace(wl.WORKLOADS[2], name="fp8-last-keys", cfg=56, n_heads=3, grid=grid, frames=14, batch=2)
+    T = w.tokens_per_frame
+    rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid, w.theta0, 0.0, None)
+    cache = swk.Cache(rope, w.batch, w.n_sink, w.n_local, torch.float8_e4m3fn, k_scale=1.0 / 64, v_scale=1.0 / 64)
+    cache.k_store.fill_(0xFF)
+    cache.v_store.fill_(0xFF)
+    k = torch.zeros((w.batch, T, w.n_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    v[:, T - 8:, :, w.head_dim - 1] = 1.0
+    q = torch.zeros_like(k)
+    o = torch.empty_like(q)
+    for f in range(w.frames):
+        swk.sa_cache_append(cache, k, v, 1, f)
+        nbytes = swk.sa_window_attn_workspace(cache, 1)
+        ws = torch.zeros(max(nbytes // 4, 4), dtype=torch.float32, device="cuda")
+        swk.sa_window_attn(cache, q, o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+        torch.cuda.synchronize()
+        got = o.float()
+        assert torch.isfinite(got).all(), f"frame {f}"
+        np.testing.assert_allclose(got[..., -1].cpu().numpy(), 8.0 / T, rtol=1e-2, err_msg=f"frame {f}")
+        assert got[..., :-1].abs().max().item() == 0.0, f"frame {f}"
+
+
 @pytest.mark.parametrize("splits", [None, "1", "5"])
 def test_fp8_attention_wan_layer(splits):
     """Wan-1.3B layer in an e4m3 cache: 3 sink + 9 local frames of 1560 tokens (24 full tiles and one of
