@@ -105,11 +105,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, ui
 // Workgroup: TM features x TN tokens, four waves in a 2 x 2 grid, each
 // (TM/2) x (TN/2) as (TM/64) x (TN/64) products of 32 x 32; two workgroups
 // per CU, so one's epilogue overlaps the other's products.  The reduction
-// runs in slices of 32: each step writes the next slice (already in
-// registers) into the free LDS stage, loads the one after into registers and
-// multiplies the current one, with one barrier per step.  Plain vector loads
-// stage the slices (the direct-to-LDS path moves far fewer bytes per cycle
-// per CU).
+// runs in slices of 64 bytes per row (32 bf16 or 64 8-bit codes): each step
+// writes the next slice (already in registers) into the free LDS stage,
+// loads the one after into registers and multiplies the current one, with
+// one barrier per step.  Plain vector loads stage the slices (the
+// direct-to-LDS path moves far fewer bytes per cycle per CU).
 template <int TM, int TN, int QT>
 __device__ __forceinline__ void proj_body(ProjArgs a) {
   constexpr int EB = QT == kOpBF16 ? 2 : 1;    // operand bytes per element
@@ -204,12 +204,6 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
 #pragma unroll
     for (int u = 0; u < kBI; ++u) st.b[64 * (wave * kBI + u) + lane] = Rb[kAI + u];
   };
-  // Slice s lives in register buffer s % kPre until it is written to LDS.
-  // Every load is unconditional (slices past the end reload the last one and
-  // are never multiplied), so inside the loop the compiler's load-completion
-  // waits stay exact: each step waits only for the slice it stores, not for
-  // the kPre - 1 slices loaded after it.
-  const int last = (nk - 1) * TKE;
   // Per-token coordinates of the tile for the cache outputs, computed once
   // here (one division per token) instead of per output piece: frame time,
   // grid row and column, and the element offsets of the token's key row and
@@ -280,6 +274,12 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
       }
     }
   }
+  // Slice s lives in register buffer s % kPre until it is written to LDS.
+  // Every load is unconditional (slices past the end reload the last one and
+  // are never multiplied), so inside the loop the compiler's load-completion
+  // waits stay exact: each step waits only for the slice it stores, not for
+  // the kPre - 1 slices loaded after it.
+  const int last = (nk - 1) * TKE;
   load_regs(R[0], 0);
   store_regs(R[0], stg[0]);
 #pragma unroll
