@@ -100,6 +100,34 @@ def traffic_from_profile(kernel_srcs):
         return None
 
 
+def sclk_under_load(launch, n_calls: int):
+    """Shader clock (MHz) that rocm-smi reports while n_calls launches run, or None."""
+    import re
+    import subprocess
+    import threading
+    import torch
+    got = {}
+
+    def sample():
+        time.sleep(0.3)
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+            m = re.search(r"sclk clock speed:\"?\s*:\s*\"\((\d+)Mhz\)", r.stdout)
+            got["mhz"] = int(m.group(1)) if m else None
+        except Exception:
+            got["mhz"] = None
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample)
+    for i in range(n_calls // 10):
+        launch(i)
+    th.start()
+    for i in range(n_calls // 10, n_calls):
+        launch(i)
+    th.join()
+    torch.cuda.synchronize()
+    return got.get("mhz")
+
+
 def cpu_baseline(w, budget_s: float):
     """The fp64 oracle as it stands, on a bounded sample of one steady-state step."""
     import numpy as np
@@ -229,13 +257,19 @@ def main():
     app_avg = sum(app_ms) / len(app_ms)
     att_avg = sum(att_ms) / len(att_ms)
 
+    # Shader clock under this load: about a second of attention calls queued,
+    # rocm-smi read once while they run (null if the tool is not there).
+    sclk_mhz = sclk_under_load(lambda i: swk.sa_window_attn(caches[i % N_LAYERS], qs[i % pool], o, 1, 0.0,
+                                                             swk.SA_MASK_FRAME_CAUSAL, ws), n_calls=6000)
+
     flops = attn_flops(T, n_win * T, H, D)
     ms_per_step = elapsed * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (att_avg * 1e-3) / 1e12
     append_bytes = 2 * 2 * T * H * D * 2  # K and V, read + write, bf16
     print(f"[bench] step {ms_per_step * 1e3:.1f} us, attention {att_avg * 1e3:.1f} us "
-          f"({achieved:.0f} TFLOP/s), append {app_avg * 1e3:.1f} us", file=sys.stderr, flush=True)
+          f"({achieved:.0f} TFLOP/s), append {app_avg * 1e3:.1f} us; shader clock under load {sclk_mhz} MHz",
+          file=sys.stderr, flush=True)
 
     # LoL diagnostic: the same attention call also reporting each row's
     # softmax mass on the sink frames (a second pass over the sink keys).
@@ -513,8 +547,11 @@ def main():
         "attention_only_latent_frames_per_s_per_layer": round(1e3 / att_avg, 1),
         "pct_bf16_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "pct_bf16_peak_attention_kernel": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "sclk_mhz_under_load": sclk_mhz,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "frac_at_measured_clock": (round(achieved / (PEAK_BF16_TFLOPS * sclk_mhz / 2400.0), 4)
+                                                if sclk_mhz else None),
                      "traffic": traffic, "kernel": "attn_bf16_kernel<128>",
                      "flops_per_launch": flops, "avg_launch_us": round(att_avg * 1e3, 2),
                      "median_launch_us": round(att_ms[len(att_ms) // 2] * 1e3, 2)},
