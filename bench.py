@@ -186,7 +186,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only (the kernels shard by head; no multi-GPU path is built); --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
     import torch
