@@ -201,3 +201,14 @@ def test_host_projection_validation():
     assert L.sa_linear(P, Q, Q, 0, 4, 64, 64, None) == _swk().SA_ERR_RANGE         # y overlaps w
     assert L.sa_linear(P, Q, R, 0, 0, 64, 64, None) == _swk().SA_OK                # nothing to do
     assert L.sa_cache_project_append(None, P, None, Q, R, 64, None, 1, 0, None) == _swk().SA_ERR_NULL
+
+
+def test_bench_rejects_more_than_one_gpu():
+    """`bench.py --gpus N` with N > 1 exits with status 2 and a JSON error line, before touching a GPU."""
+    import json
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
