@@ -293,7 +293,8 @@ sa_status sa_window_attn_workspace(const sa_cache* cache, int32_t n_q, size_t* b
  *         the key-split partial results of this call only and needs no
  *         initialisation.  Calls sharing a workspace must not run
  *         concurrently (stream order is enough).
- * o must not alias q. */
+ * q, o, the workspace and the cache's two stores must not overlap one
+ * another (SA_ERR_RANGE, nothing launched). */
 sa_status sa_window_attn(const sa_cache* cache, const void* q, void* o, int32_t n_q, float scale,
                          sa_mask mask, void* workspace, size_t workspace_bytes, void* stream);
 

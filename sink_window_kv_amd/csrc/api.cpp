@@ -57,6 +57,12 @@ sa_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Do the byte ranges [p, p + pb) and [q, q + qb) share a byte?
+bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+  return pb > 0 && qb > 0 && a0 < b0 + qb && b0 < a0 + pb;
+}
+
 size_t elem_size(sa_dtype d) { return d == SA_FP8 ? 1 : (d == SA_BF16 ? 2 : 4); }
 
 sa_status hip_fail(hipError_t e, const char* what) {
@@ -430,10 +436,6 @@ sa_status sa_linear(const void* x, const void* w, void* y, sa_dtype dtype, int64
     return fail(SA_ERR_SHAPE, "out_features must be a multiple of 16 in [16, 2^20]");
   if (sa_status s = check_proj_sizes(n_rows, in_features, out_features, elem_size(dtype))) return s;
   const size_t es = elem_size(dtype);
-  const auto overlaps = [](const void* p, size_t pb, const void* q, size_t qb) {
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
-    return a0 < b0 + qb && b0 < a0 + pb;
-  };
   const size_t yb = static_cast<size_t>(n_rows) * out_features * es;
   if (n_rows > 0 && (overlaps(y, yb, x, static_cast<size_t>(n_rows) * in_features * es) ||
                      overlaps(y, yb, w, static_cast<size_t>(out_features) * in_features * es)))
@@ -492,10 +494,6 @@ sa_status sa_linear_q8(const void* x_codes, const float* x_scales, const void* w
     return fail(SA_ERR_SHAPE, "out_features must be a multiple of 16 in [16, 2^20]");
   if (sa_status s = check_q8_hidden(in_features)) return s;
   if (sa_status s = check_proj_sizes(n_rows, in_features, out_features, 1)) return s;
-  const auto overlaps = [](const void* p, size_t pb, const void* q, size_t qb) {
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
-    return a0 < b0 + qb && b0 < a0 + pb;
-  };
   const size_t yb = static_cast<size_t>(n_rows) * out_features * 2;
   if (n_rows > 0 && (overlaps(y, yb, x_codes, static_cast<size_t>(n_rows) * in_features) ||
                      overlaps(y, yb, w_codes, static_cast<size_t>(out_features) * in_features) ||
@@ -629,6 +627,18 @@ sa_status check_attn(const sa_cache* c, const void* q, void* o, int32_t n_q, flo
   if (sa_status s = attn_plan(c, n_q, &splits, &need)) return s;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SA_ERR_RANGE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  // q and o [B, n_q*T, H, D]; o, q and the workspace must be disjoint from
+  // each other and from the cache's stores.
+  const size_t io = static_cast<size_t>(c->desc.batch) * n_q * c->desc.tokens_per_frame * c->desc.n_heads *
+                    c->desc.head_dim * (c->desc.dtype == SA_F32 ? 4 : 2);
+  const size_t sb = sa_cache_store_bytes(&c->desc);
+  if (overlaps(o, io, q, io)) return fail(SA_ERR_RANGE, "o must not overlap q");
+  if (overlaps(o, io, c->desc.k_store, sb) || overlaps(o, io, c->desc.v_store, sb) ||
+      overlaps(q, io, c->desc.k_store, sb) || overlaps(q, io, c->desc.v_store, sb))
+    return fail(SA_ERR_RANGE, "q and o must not overlap the cache stores");
+  if (need > 0 && (overlaps(workspace, need, q, io) || overlaps(workspace, need, o, io) ||
+                   overlaps(workspace, need, c->desc.k_store, sb) || overlaps(workspace, need, c->desc.v_store, sb)))
+    return fail(SA_ERR_RANGE, "the workspace must not overlap q, o or the cache stores");
   return SA_OK;
 }
 

@@ -383,6 +383,40 @@ def test_attention_errors():
     assert e.value.status == swk.SA_ERR_RANGE
 
 
+def test_attention_rejects_overlapping_buffers():
+    """o, q, the workspace and the cache stores must be disjoint; every overlap is SA_ERR_RANGE before any launch."""
+    import torch
+    swk = _swk()
+    w = wl.WORKLOADS[2]
+    gs = GpuStream(w, with_oracle=False)
+    shape = (1, w.tokens_per_frame, w.n_heads, w.head_dim)
+    n = w.tokens_per_frame * w.n_heads * w.head_dim
+    z = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    swk.sa_cache_append(gs.cache, z, z, 1, 0)
+    need = swk.sa_window_attn_workspace(gs.cache, 1)
+    ws_n = max(need // 4, 4)
+    ws = torch.zeros(ws_n, dtype=torch.float32, device="cuda")
+
+    def rejected(q, o, workspace):
+        with pytest.raises(swk.SinkAttnError) as e:
+            swk.sa_window_attn(gs.cache, q, o, 1, workspace=workspace)
+        assert e.value.status == swk.SA_ERR_RANGE
+
+    big = torch.zeros(2 * n, dtype=torch.bfloat16, device="cuda")
+    rejected(big[:n].view(shape), big[n // 2:n // 2 + n].view(shape), ws)      # o overlaps half of q
+    rejected(z, gs.cache.k_store[:n].view(shape), ws)                         # o is the key store
+    rejected(gs.cache.v_store[:n].view(shape), torch.empty_like(z), ws)       # q is the value store
+    if need > 0:
+        o_ws = torch.zeros(2 * n + 2 * ws_n, dtype=torch.bfloat16, device="cuda")
+        o = o_ws[:n].view(shape)
+        rejected(z, o, o_ws[n // 2:n // 2 + 2 * ws_n].view(torch.float32))    # workspace overlaps o
+        rejected(z, torch.empty_like(z), gs.cache.k_store[:2 * ws_n].view(torch.float32))  # workspace is the store
+    o = torch.empty_like(z)
+    swk.sa_window_attn(gs.cache, z, o, 1, workspace=ws)                       # disjoint buffers: accepted
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_workspace_too_small_is_rejected():
     import torch
     swk = _swk()
