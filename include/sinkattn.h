@@ -303,7 +303,8 @@ sa_status sa_window_attn(const sa_cache* cache, const void* q, void* o, int32_t 
  * frames).  Same arguments, workspace and output o as sa_window_attn, plus
  *   sink_mass [B, n_q*T_f, H] fp32: for each query row and head, the softmax
  *             probability mass the row puts on the keys of the resident sink
- *             frames (0 when no sink frame is resident).
+ *             frames (0 when no sink frame is resident); it must not
+ *             overlap q, o, the workspace or the stores (SA_ERR_RANGE).
  * It runs the attention, which also records each row's log-sum-exp, then the
  * same rows over the sink keys only (about n_sink / (n_sink + n_local) of the
  * attention's work); mass = exp(LSE_sinks - LSE_all). */

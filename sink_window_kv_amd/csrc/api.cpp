@@ -688,6 +688,20 @@ sa_status sa_window_attn_sink_mass(const sa_cache* c, const void* q, void* o, fl
   if (c && c->desc.dtype == SA_FP8) return fail(SA_ERR_DTYPE, "the sink mass is not supported for an SA_FP8 cache");
   if (!aligned16(sink_mass)) return fail(SA_ERR_ALIGN, "sink_mass must be 16-byte aligned");
   if (sa_status s = check_attn(c, q, o, n_q, scale, mask, workspace, workspace_bytes)) return s;
+  {
+    // sink_mass [B, n_q*T, H] fp32 is a fourth output: disjoint from q, o, the workspace and the stores
+    const size_t rows = static_cast<size_t>(c->desc.batch) * n_q * c->desc.tokens_per_frame * c->desc.n_heads;
+    const size_t io = rows * c->desc.head_dim * (c->desc.dtype == SA_F32 ? 4 : 2);
+    const size_t sb = sa_cache_store_bytes(&c->desc);
+    int splits = 1;
+    size_t need = 0;
+    (void)attn_plan(c, n_q, &splits, &need);
+    const size_t mb = rows * sizeof(float);
+    if (overlaps(sink_mass, mb, q, io) || overlaps(sink_mass, mb, o, io) ||
+        (need > 0 && overlaps(sink_mass, mb, workspace, need)) || overlaps(sink_mass, mb, c->desc.k_store, sb) ||
+        overlaps(sink_mass, mb, c->desc.v_store, sb))
+      return fail(SA_ERR_RANGE, "sink_mass must not overlap q, o, the workspace or the cache stores");
+  }
   sa::AttnArgs a = attn_args(c, q, o, n_q, scale, mask, workspace);
   int n_sink_res = 0;
   for (const auto& f : c->plan.resident()) n_sink_res += f.segment == 0 ? 1 : 0;

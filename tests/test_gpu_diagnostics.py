@@ -111,3 +111,8 @@ def test_sink_mass_f32_and_no_sinks():
     with pytest.raises(swk.SinkAttnError) as e:
         swk.sa_window_attn_sink_mass(gs0.cache, q, o, None, 1)
     assert e.value.status == swk.SA_ERR_NULL
+    rows = q.shape[1] * q.shape[2]
+    for target in (o, q, gs0.cache.k_store):          # sink_mass placed on another buffer
+        with pytest.raises(swk.SinkAttnError) as e:
+            swk.sa_window_attn_sink_mass(gs0.cache, q, o, target.view(-1)[:2 * rows].view(torch.float32), 1)
+        assert e.value.status == swk.SA_ERR_RANGE
