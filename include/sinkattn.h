@@ -32,6 +32,9 @@
  * - Handles are not thread-safe; distinct handles are independent.  A handle
  *   is bound to the device that was current at its creation.
  * - Alignment: every device pointer must be 16-byte aligned.
+ * - A cache call's inputs and outputs must not overlap the cache's own two
+ *   stores, and an output must not overlap that call's inputs
+ *   (SA_ERR_RANGE, nothing changed or launched).
  */
 #ifndef SINKATTN_H
 #define SINKATTN_H

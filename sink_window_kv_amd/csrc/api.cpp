@@ -179,6 +179,12 @@ sa_status check_proj_sizes(int64_t n_tok, int32_t hidden, int32_t width, size_t 
 int proj_dtype(const sa_cache* c) { return c->desc.dtype == SA_FP8 ? sa::kBF16 : static_cast<int>(c->desc.dtype); }
 size_t proj_elem_size(const sa_cache* c) { return c->desc.dtype == SA_F32 ? 4 : 2; }
 
+// Does [p, p + bytes) share a byte with either of the cache's stores?
+bool hits_stores(const sa_cache* c, const void* p, size_t bytes) {
+  const size_t sb = sa_cache_store_bytes(&c->desc);
+  return overlaps(p, bytes, c->desc.k_store, sb) || overlaps(p, bytes, c->desc.v_store, sb);
+}
+
 // Projection segments into this cache: [q rows,] rotated keys, values.
 sa::ProjArgs cache_proj_args(const sa_cache* c, const void* x, const void* w_q, void* q_out, const void* w_k,
                              const void* w_v, int32_t hidden) {
@@ -381,6 +387,10 @@ sa_status sa_cache_append(sa_cache* c, const void* k, const void* v, int32_t n_f
   if (!aligned16(k) || !aligned16(v)) return fail(SA_ERR_ALIGN, "k and v must be 16-byte aligned");
   if (t0 < 0 || t0 > (int64_t(1) << 40)) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40]");
   if (sa_status s = check_append_chunk(c, n_frames, t0)) return s;
+  const size_t in_bytes = static_cast<size_t>(c->desc.batch) * n_frames * c->desc.tokens_per_frame * c->desc.n_heads *
+                          c->desc.head_dim * proj_elem_size(c);
+  if (hits_stores(c, k, in_bytes) || hits_stores(c, v, in_bytes))
+    return fail(SA_ERR_RANGE, "k and v must not overlap the cache stores");
   const sa::FrameTable chunk = chunk_table(c, n_frames, t0);
   const hipError_t e = sa::launch_append(rope_args(c->rope), geom(c), k, v, c->desc.dtype, chunk,
                                          static_cast<hipStream_t>(stream));
@@ -398,6 +408,11 @@ sa_status sa_cache_recache(sa_cache* c, const void* x, const void* w_k, const vo
   if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "recache on an empty cache");
   const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * c->plan.resident().size() * c->desc.tokens_per_frame;
   if (sa_status s = check_proj_sizes(n_tok, hidden, hd, proj_elem_size(c))) return s;
+  {
+    const size_t es = proj_elem_size(c), wb = static_cast<size_t>(hd) * hidden * es;
+    if (hits_stores(c, x, static_cast<size_t>(n_tok) * hidden * es) || hits_stores(c, w_k, wb) || hits_stores(c, w_v, wb))
+      return fail(SA_ERR_RANGE, "x and the weights must not overlap the cache stores");
+  }
   sa::ProjArgs a = cache_proj_args(c, x, nullptr, nullptr, w_k, w_v, hidden);
   a.n_tok = n_tok;
   a.frames = resident_table(c);
@@ -417,6 +432,16 @@ sa_status sa_cache_project_append(sa_cache* c, const void* x, const void* w_q, c
   const int hd = c->desc.n_heads * c->desc.head_dim;
   const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * n_frames * c->desc.tokens_per_frame;
   if (sa_status s = check_proj_sizes(n_tok, hidden, hd, proj_elem_size(c))) return s;
+  {
+    const size_t es = proj_elem_size(c), wb = static_cast<size_t>(hd) * hidden * es;
+    const size_t xb = static_cast<size_t>(n_tok) * hidden * es, qb = q_out ? static_cast<size_t>(n_tok) * hd * es : 0;
+    if (hits_stores(c, x, xb) || hits_stores(c, w_k, wb) || hits_stores(c, w_v, wb) ||
+        (w_q && hits_stores(c, w_q, wb)) || (q_out && hits_stores(c, q_out, qb)))
+      return fail(SA_ERR_RANGE, "x, the weights and q_out must not overlap the cache stores");
+    if (q_out && (overlaps(q_out, qb, x, xb) || overlaps(q_out, qb, w_q, wb) || overlaps(q_out, qb, w_k, wb) ||
+                  overlaps(q_out, qb, w_v, wb)))
+      return fail(SA_ERR_RANGE, "q_out must not overlap x or the weights");
+  }
   sa::ProjArgs a = cache_proj_args(c, x, w_q, q_out, w_k, w_v, hidden);
   a.n_tok = n_tok;
   a.frames = chunk_table(c, n_frames, t0);
@@ -539,6 +564,13 @@ sa_status sa_cache_recache_q8(sa_cache* c, const void* x_codes, const float* x_s
   if (!c->plan.has_frames()) return fail(SA_ERR_STATE, "recache on an empty cache");
   const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * c->plan.resident().size() * c->desc.tokens_per_frame;
   if (sa_status s = check_proj_sizes(n_tok, hidden, hd, 1)) return s;
+  {
+    const size_t wb = static_cast<size_t>(hd) * hidden, ws = static_cast<size_t>(hd) * 4;
+    if (hits_stores(c, x_codes, static_cast<size_t>(n_tok) * hidden) || hits_stores(c, x_scales, static_cast<size_t>(n_tok) * 4) ||
+        hits_stores(c, wk_codes, wb) || hits_stores(c, wk_scales, ws) || hits_stores(c, wv_codes, wb) ||
+        hits_stores(c, wv_scales, ws))
+      return fail(SA_ERR_RANGE, "codes and scales must not overlap the cache stores");
+  }
   sa::ProjArgs a = cache_proj_args(c, x_codes, nullptr, nullptr, wk_codes, wv_codes, hidden);
   a.w_scale[0] = wk_scales;
   a.w_scale[1] = a.w_scale[2] = wv_scales;
@@ -570,6 +602,21 @@ sa_status sa_cache_project_append_q8(sa_cache* c, const void* x_codes, const flo
   const int hd = c->desc.n_heads * c->desc.head_dim;
   const int64_t n_tok = static_cast<int64_t>(c->desc.batch) * n_frames * c->desc.tokens_per_frame;
   if (sa_status s = check_proj_sizes(n_tok, hidden, hd, 1)) return s;
+  {
+    const size_t xb = static_cast<size_t>(n_tok) * hidden, wb = static_cast<size_t>(hd) * hidden;
+    const size_t xs = static_cast<size_t>(n_tok) * 4, ws = static_cast<size_t>(hd) * 4;
+    const size_t qb = q_out ? static_cast<size_t>(n_tok) * hd * 2 : 0;
+    if (hits_stores(c, x_codes, xb) || hits_stores(c, x_scales, xs) || hits_stores(c, wk_codes, wb) ||
+        hits_stores(c, wk_scales, ws) || hits_stores(c, wv_codes, wb) || hits_stores(c, wv_scales, ws) ||
+        (wq_codes && (hits_stores(c, wq_codes, wb) || hits_stores(c, wq_scales, ws))) ||
+        (q_out && hits_stores(c, q_out, qb)))
+      return fail(SA_ERR_RANGE, "codes, scales and q_out must not overlap the cache stores");
+    if (q_out && (overlaps(q_out, qb, x_codes, xb) || overlaps(q_out, qb, x_scales, xs) ||
+                  overlaps(q_out, qb, wq_codes, wb) || overlaps(q_out, qb, wq_scales, ws) ||
+                  overlaps(q_out, qb, wk_codes, wb) || overlaps(q_out, qb, wk_scales, ws) ||
+                  overlaps(q_out, qb, wv_codes, wb) || overlaps(q_out, qb, wv_scales, ws)))
+      return fail(SA_ERR_RANGE, "q_out must not overlap the codes or scales");
+  }
   sa::ProjArgs a = cache_proj_args(c, x_codes, wq_codes, q_out, wk_codes, wv_codes, hidden);
   int n = 0;
   if (wq_codes) a.w_scale[n++] = wq_scales;
@@ -749,6 +796,10 @@ sa_status sa_cache_read(const sa_cache* c, int32_t index, void* k_out, void* v_o
   const auto res = c->plan.resident();
   if (index < 0 || index >= static_cast<int32_t>(res.size()))
     return fail(SA_ERR_RANGE, "index %d outside the %d resident frames", index, static_cast<int>(res.size()));
+  const size_t ob = static_cast<size_t>(c->desc.batch) * c->desc.tokens_per_frame * c->desc.n_heads * c->desc.head_dim *
+                    elem_size(c->desc.dtype);
+  if ((k_out && hits_stores(c, k_out, ob)) || (v_out && hits_stores(c, v_out, ob)))
+    return fail(SA_ERR_RANGE, "k_out and v_out must not overlap the cache stores");
   const hipError_t e = sa::launch_read(geom(c), res[index].store_slot, k_out, v_out, c->desc.dtype,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "read launch");

@@ -132,6 +132,44 @@ def test_project_append_without_q_and_errors():
         assert swk.sa_cache_counts(gs.cache) == before
 
 
+def test_cache_calls_reject_buffers_on_the_stores():
+    """Inputs and outputs placed on the cache's own stores (or q_out on x) are SA_ERR_RANGE, cache unchanged."""
+    import torch
+    swk = _swk()
+    w = SMALL
+    gs = GpuStream(w, with_oracle=False)
+    wq, wk, wv = wl.projection_weights(w)
+    dq, dk, dv = _weights_dev((wq, wk, wv), w.dtype)
+    T = w.tokens_per_frame
+    shape = (w.batch, T, w.n_heads, w.head_dim)
+    n = w.batch * T * w.n_heads * w.head_dim
+    tx = to_dev(wl.frame_hidden(w, 0, 1), w.dtype)
+    swk.sa_cache_project_append(gs.cache, tx, None, dk, dv, w.hidden, None, 1, 0)
+    torch.cuda.synchronize()
+    before = swk.sa_cache_counts(gs.cache)
+    ks, vs = gs.cache.k_store, gs.cache.v_store
+    z = torch.zeros(shape, dtype=ks.dtype, device="cuda")
+    nx = tx.numel()
+    buf = torch.zeros(nx + n, dtype=tx.dtype, device="cuda")
+    x2 = buf[:nx].view(tx.shape)
+    x2.copy_(tx)
+    q_on_x = buf[nx // 2:nx // 2 + n].view(shape)
+    calls = [
+        lambda: swk.sa_cache_append(gs.cache, ks[:n].view(shape), z, 1, 1),                   # k on the key store
+        lambda: swk.sa_cache_append(gs.cache, z, vs[n:2 * n].view(shape), 1, 1),              # v on the value store
+        lambda: swk.sa_cache_read(gs.cache, 0, k_out=vs[:n].view(shape)),                     # read into a store
+        lambda: swk.sa_cache_recache(gs.cache, ks[:nx].view(tx.shape), dk, dv, w.hidden),     # x on the key store
+        lambda: swk.sa_cache_project_append(gs.cache, tx, None, dk, vs[:dv.numel()].view(dv.shape), w.hidden, None,
+                                            1, 1),                                           # w_v on the value store
+        lambda: swk.sa_cache_project_append(gs.cache, x2, dq, dk, dv, w.hidden, q_on_x, 1, 1),  # q_out on x
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(swk.SinkAttnError) as ei:
+            call()
+        assert ei.value.status == swk.SA_ERR_RANGE, i
+        assert swk.sa_cache_counts(gs.cache) == before, i
+
+
 @pytest.mark.parametrize("n_rows,fin,fout,dtype", [
     (1560, 1536, 1536, "bf16"),   # the output projection of one Wan-1.3B frame
     (333, 96, 80, "bf16"),        # ragged rows, 80 outputs (padding in every tile shape)
