@@ -103,6 +103,12 @@ typedef struct {
   const double* eps;    /* host [H], each in [-1, 1]; NULL = no jitter; copied */
   uint32_t jitter_axes; /* SA_AXIS_* bitmask; 0 is treated as SA_AXIS_T */
   double t_scale;       /* time-position scale (PI); 0 is treated as 1; else finite, > 0 */
+  /* Optional per-head, per-axis bases, host [H*3] in (t, h, w) order per
+   * head, each finite and > 1; copied.  When non-NULL it is theta_hat itself
+   * ([LoL] "method steps" (4)) and theta0, sigma, eps and jitter_axes are
+   * ignored, so any per-axis base can be expressed; NULL = build theta_hat
+   * from theta0, sigma, eps and jitter_axes as above. */
+  const double* theta;
 } sa_rope_desc;
 
 typedef struct sa_rope sa_rope;
@@ -121,7 +127,8 @@ sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out);
 void sa_rope_destroy(sa_rope* rope);
 
 /* y = RoPE(x) for n_frames latent frames: x, y [B, n_frames*T_f, H, D] of
- * dtype; frame j of the token axis has time t0 + j.  y may alias x exactly. */
+ * dtype; frame j of the token axis has time t0 + j.  y may be x itself
+ * (in place); any other overlap of y with x is SA_ERR_RANGE. */
 sa_status sa_rope3d_apply(const sa_rope* rope, const void* x, void* y, sa_dtype dtype,
                           int32_t batch, int32_t n_frames, int64_t t0, void* stream);
 
@@ -169,6 +176,9 @@ typedef struct {
 
 /* Bytes of ONE store (k or v) for desc; 0 if desc is invalid. */
 size_t sa_cache_store_bytes(const sa_cache_desc* desc);
+/* The same number under its short name: the caller allocates k_store and
+ * v_store of sa_cache_bytes(desc) bytes each. */
+size_t sa_cache_bytes(const sa_cache_desc* desc);
 
 /* Host metadata only; makes no HIP call.  rope must outlive the cache. */
 sa_status sa_cache_create(const sa_cache_desc* desc, const sa_rope* rope, sa_cache** out);
@@ -251,7 +261,8 @@ typedef enum { SA_Q_INT8 = 0, SA_Q_E4M3 = 1 } sa_qtype;
  * [F][C] (per output feature) alike.
  *   x [n_rows, n_cols] bf16 (finite); codes [n_rows, n_cols] bytes (int8 or
  *   e4m3); scales [n_rows] fp32.  n_cols a multiple of 8 in [8, 65536];
- *   n_rows >= 0 (0 launches nothing). */
+ *   n_rows >= 0 (0 launches nothing).  x, codes and scales must not overlap
+ *   one another (SA_ERR_RANGE). */
 sa_status sa_quantize_rows(const void* x, void* codes, float* scales, sa_qtype qtype, int64_t n_rows,
                            int32_t n_cols, void* stream);
 
@@ -336,6 +347,20 @@ sa_status sa_cache_read(const sa_cache* cache, int32_t index, void* k_out, void*
 
 /* Number of frames appended since creation / reset, and resident now. */
 sa_status sa_cache_counts(const sa_cache* cache, int64_t* n_appended, int32_t* n_resident);
+
+/* Test and tuning hook: force a launch shape for every later call in this
+ * process, in place of the automatic choice (value 0 restores it).  Results
+ * stay within the same tolerances whatever the shape; the parity tests use
+ * this to cover every shape the automatic choice can take.  Not synchronised
+ * with calls running on other host threads.
+ *   SA_KNOB_ATTN_WAVES   waves per bf16 attention workgroup: 4 or 8
+ *   SA_KNOB_ATTN_SPLITS  key splits of the bf16 / e4m3 attention: 1 .. 16
+ *                        (capped at one split per 8 key tiles)
+ *   SA_KNOB_PROJ_TILE    projection GEMM tile (features x tokens):
+ *                        1 = 256 x 128, 2 = 128 x 128, 3 = 128 x 64
+ * SA_ERR_RANGE for an unknown knob or a value outside its set. */
+typedef enum { SA_KNOB_ATTN_WAVES = 0, SA_KNOB_ATTN_SPLITS = 1, SA_KNOB_PROJ_TILE = 2 } sa_knob;
+sa_status sa_set_launch_override(sa_knob knob, int32_t value);
 
 const char* sa_status_str(sa_status status);
 const char* sa_last_error(void); /* thread-local, "" when none */

@@ -21,6 +21,7 @@ SA_MASK_NONE, SA_MASK_FRAME_CAUSAL = 0, 1
 SA_AXIS_T, SA_AXIS_H, SA_AXIS_W = 1, 2, 4
 SA_Q_INT8, SA_Q_E4M3 = 0, 1
 SA_MAX_FRAMES = 64
+SA_KNOB_ATTN_WAVES, SA_KNOB_ATTN_SPLITS, SA_KNOB_PROJ_TILE = 0, 1, 2
 
 
 class SinkAttnError(RuntimeError):
@@ -39,7 +40,7 @@ class sa_rope_desc(ctypes.Structure):
                 ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
                 ("theta0", ctypes.c_double), ("sigma", ctypes.c_double),
                 ("eps", ctypes.POINTER(ctypes.c_double)), ("jitter_axes", ctypes.c_uint32),
-                ("t_scale", ctypes.c_double)]
+                ("t_scale", ctypes.c_double), ("theta", ctypes.POINTER(ctypes.c_double))]
 
 
 class sa_cache_desc(ctypes.Structure):
@@ -63,6 +64,8 @@ _SIGNATURES = {
     "sa_rope3d_apply": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int64, _VP]),
     "sa_cache_store_bytes": (ctypes.c_size_t, [ctypes.POINTER(sa_cache_desc)]),
+    "sa_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(sa_cache_desc)]),
+    "sa_set_launch_override": (ctypes.c_int, [ctypes.c_int, ctypes.c_int32]),
     "sa_cache_create": (ctypes.c_int, [ctypes.POINTER(sa_cache_desc), _VP, ctypes.POINTER(_VP)]),
     "sa_cache_destroy": (None, [_VP]),
     "sa_cache_reset": (ctypes.c_int, [_VP]),
@@ -147,25 +150,37 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale=1.0):
+def _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale=1.0, theta=None):
+    """theta: optional per-head, per-axis bases [H][3] (t, h, w); replaces theta0/sigma/eps/jitter_axes."""
     d = sa_rope_desc()
     d.n_heads, d.head_dim = n_heads, head_dim
     d.dim_t, d.dim_h, d.dim_w = dims
     d.grid_h, d.grid_w = grid
     d.theta0, d.sigma = float(theta0), float(sigma)
-    keep = None
+    keep = []
     if eps is not None:
-        keep = (ctypes.c_double * n_heads)(*[float(e) for e in eps])
-        d.eps = ctypes.cast(keep, ctypes.POINTER(ctypes.c_double))
+        keep.append((ctypes.c_double * n_heads)(*[float(e) for e in eps]))
+        d.eps = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_double))
+    if theta is not None:
+        flat = [float(x) for row in theta for x in row]
+        if len(flat) != 3 * n_heads:
+            raise ValueError("theta must hold 3 bases per head")
+        keep.append((ctypes.c_double * (3 * n_heads))(*flat))
+        d.theta = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_double))
     d.jitter_axes = jitter_axes
     d.t_scale = float(t_scale)
     return d, keep
 
 
+def sa_set_launch_override(knob: int, value: int):
+    """Test / tuning hook: force a launch shape (0 = automatic); see the header."""
+    _check(lib().sa_set_launch_override(knob, value), "sa_set_launch_override")
+
+
 def sa_rope_tables(n_heads, head_dim, dims, grid, theta0=10000.0, sigma=0.0, eps=None,
-                   jitter_axes=SA_AXIS_T, t_scale=1.0):
+                   jitter_axes=SA_AXIS_T, t_scale=1.0, theta=None):
     """Host-only tables: (theta_hat [H][3], freq [H][D/2]) as nested lists of floats."""
-    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale)
+    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale, theta)
     th = (ctypes.c_double * (n_heads * 3))()
     fr = (ctypes.c_double * (n_heads * head_dim // 2))()
     _check(lib().sa_rope_tables(ctypes.byref(d), th, fr), "sa_rope_tables")
@@ -177,9 +192,9 @@ class Rope:
     """Owns an sa_rope handle (per-head fp64 frequency table on the device)."""
 
     def __init__(self, n_heads, head_dim, dims, grid, theta0=10000.0, sigma=0.0, eps=None,
-                 jitter_axes=SA_AXIS_T, t_scale=1.0):
+                 jitter_axes=SA_AXIS_T, t_scale=1.0, theta=None):
         self.n_heads, self.head_dim, self.dims, self.grid = n_heads, head_dim, tuple(dims), tuple(grid)
-        d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale)
+        d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale, theta)
         h = _VP()
         _check(lib().sa_rope_create(ctypes.byref(d), ctypes.byref(h)), "sa_rope_create")
         self.handle = h
@@ -333,9 +348,9 @@ def sa_window_attn_sink_mass(cache: Cache, q, o, sink_mass, n_q: int, scale: flo
 
 
 def sa_rope_phase_coherence(n_heads, head_dim, dims, grid, deltas: Sequence[float], theta0=10000.0, sigma=0.0,
-                            eps=None, jitter_axes=SA_AXIS_T, t_scale=1.0):
+                            eps=None, jitter_axes=SA_AXIS_T, t_scale=1.0, theta=None):
     """Host-only C_h(delta) over each head's time-axis frequencies: list (per head) of complex values."""
-    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale)
+    d, _keep = _rope_desc(n_heads, head_dim, dims, grid, theta0, sigma, eps, jitter_axes, t_scale, theta)
     n = len(deltas)
     dl = (ctypes.c_double * max(n, 1))(*[float(x) for x in deltas])
     re = (ctypes.c_double * max(n_heads * n, 1))()

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -39,6 +40,9 @@ struct sa_cache {
 namespace {
 
 thread_local std::string g_last_error;
+
+// Launch-shape overrides (sa_set_launch_override); 0 = automatic.
+std::atomic<int> g_knobs[sa::kNumKnobs];
 
 sa_status fail(sa_status s, const char* fmt, ...) {
   char buf[512];
@@ -82,11 +86,17 @@ sa_status check_rope_desc(const sa_rope_desc* d) {
   if (d->grid_h < 1 || d->grid_w < 1) return fail(SA_ERR_SHAPE, "grid must be >= 1x1");
   const long long tf = static_cast<long long>(d->grid_h) * d->grid_w;
   if (tf % 8 != 0 || tf > (1 << 20)) return fail(SA_ERR_SHAPE, "tokens per frame must be a multiple of 8 and <= 2^20");
+  if (d->t_scale != 0.0 && !(d->t_scale > 0.0 && std::isfinite(d->t_scale)))
+    return fail(SA_ERR_RANGE, "t_scale must be 0 (none) or finite and > 0");
+  if (d->theta) {  // theta_hat given per head and axis: theta0, sigma, eps and jitter_axes are unused
+    for (int i = 0; i < d->n_heads * 3; ++i)
+      if (!(d->theta[i] > 1.0) || !std::isfinite(d->theta[i]))
+        return fail(SA_ERR_RANGE, "theta[%d] (head %d, axis %d) must be finite and > 1", i, i / 3, i % 3);
+    return SA_OK;
+  }
   if (!(d->theta0 > 1.0) || !std::isfinite(d->theta0)) return fail(SA_ERR_RANGE, "theta0 must be finite and > 1");
   if (!(d->sigma >= 0.0) || !std::isfinite(d->sigma)) return fail(SA_ERR_RANGE, "sigma must be finite and >= 0");
   if (d->jitter_axes > 7u) return fail(SA_ERR_RANGE, "jitter_axes must be a SA_AXIS_* mask");
-  if (d->t_scale != 0.0 && !(d->t_scale > 0.0 && std::isfinite(d->t_scale)))
-    return fail(SA_ERR_RANGE, "t_scale must be 0 (none) or finite and > 0");
   if (d->eps) {
     for (int h = 0; h < d->n_heads; ++h) {
       const double e = d->eps[h];
@@ -235,13 +245,26 @@ const char* sa_status_str(sa_status s) {
 
 const char* sa_last_error(void) { return g_last_error.c_str(); }
 
+sa_status sa_set_launch_override(sa_knob knob, int32_t value) {
+  bool valid = false;
+  switch (knob) {
+    case SA_KNOB_ATTN_WAVES: valid = value == 0 || value == 4 || value == 8; break;
+    case SA_KNOB_ATTN_SPLITS: valid = value >= 0 && value <= 16; break;
+    case SA_KNOB_PROJ_TILE: valid = value >= 0 && value <= 3; break;
+    default: return fail(SA_ERR_RANGE, "unknown launch knob %d", static_cast<int>(knob));
+  }
+  if (!valid) return fail(SA_ERR_RANGE, "value %d is outside the set of knob %d", value, static_cast<int>(knob));
+  g_knobs[knob].store(value, std::memory_order_relaxed);
+  return ok();
+}
+
 const char* sa_version(void) { return "libsinkattn 0.1 (gfx950)"; }
 
 sa_status sa_rope_tables(const sa_rope_desc* desc, double* theta_hat_out, double* freq_out) {
   if (sa_status s = check_rope_desc(desc)) return s;
   const int dims[3] = {desc->dim_t, desc->dim_h, desc->dim_w};
   const sa::RopeTables t = sa::build_rope_tables(desc->n_heads, desc->head_dim, dims, desc->theta0,
-                                                 desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale);
+                                                 desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale, desc->theta);
   if (theta_hat_out) std::memcpy(theta_hat_out, t.theta_hat.data(), t.theta_hat.size() * sizeof(double));
   if (freq_out) std::memcpy(freq_out, t.freq.data(), t.freq.size() * sizeof(double));
   return ok();
@@ -254,7 +277,7 @@ sa_status sa_rope_phase_coherence(const sa_rope_desc* desc, const double* deltas
   if (desc->dim_t == 0) return fail(SA_ERR_SHAPE, "no time-axis channels (dim_t is 0)");
   const int dims[3] = {desc->dim_t, desc->dim_h, desc->dim_w};
   const sa::RopeTables t = sa::build_rope_tables(desc->n_heads, desc->head_dim, dims, desc->theta0,
-                                                 desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale);
+                                                 desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale, desc->theta);
   const int half = desc->head_dim / 2;
   const int K = desc->dim_t / 2;  // time pairs come first in every head's table
   for (int h = 0; h < desc->n_heads; ++h)
@@ -284,9 +307,9 @@ sa_status sa_rope_create(const sa_rope_desc* desc, sa_rope** out) {
   r->grid_h = desc->grid_h;
   r->grid_w = desc->grid_w;
   r->tables = sa::build_rope_tables(desc->n_heads, desc->head_dim, r->dims, desc->theta0,
-                                    desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale);
+                                    desc->sigma, desc->eps, desc->jitter_axes, desc->t_scale, desc->theta);
   r->grid_table = sa::build_rope_grid_table(r->tables, desc->n_heads, desc->head_dim, r->dims, desc->grid_h,
-                                            desc->grid_w, desc->jitter_axes);
+                                            desc->grid_w);
   hipError_t e = hipGetDevice(&r->device);
   if (e == hipSuccess) e = hipMalloc(&r->d_freq, r->tables.freq.size() * sizeof(double));
   if (e == hipSuccess)
@@ -323,12 +346,17 @@ sa_status sa_rope3d_apply(const sa_rope* rope, const void* x, void* y, sa_dtype 
   if (!aligned16(x) || !aligned16(y)) return fail(SA_ERR_ALIGN, "x and y must be 16-byte aligned");
   if (t0 < 0 || t0 > (int64_t(1) << 40) - n_frames) return fail(SA_ERR_RANGE, "t0 out of range [0, 2^40)");
   const int T = rope->grid_h * rope->grid_w;
+  const size_t bytes = static_cast<size_t>(batch) * n_frames * T * rope->n_heads * rope->head_dim * elem_size(dtype);
+  if (x != y && overlaps(x, bytes, y, bytes))
+    return fail(SA_ERR_RANGE, "y must be x itself or not overlap it");
   const hipError_t e = sa::launch_rope3d(rope_args(rope), x, y, dtype, batch, rope->n_heads,
                                          rope->head_dim, T, n_frames, t0,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rope3d launch");
   return ok();
 }
+
+size_t sa_cache_bytes(const sa_cache_desc* d) { return sa_cache_store_bytes(d); }
 
 size_t sa_cache_store_bytes(const sa_cache_desc* d) {
   if (!d || d->batch < 1 || d->n_heads < 1 || (d->head_dim != 64 && d->head_dim != 128) ||
@@ -501,6 +529,13 @@ sa_status sa_quantize_rows(const void* x, void* codes, float* scales, sa_qtype q
   if (n_rows < 0) return fail(SA_ERR_SHAPE, "n_rows must be >= 0");
   if (n_cols < 8 || n_cols % 8 != 0 || n_cols > (1 << 16))
     return fail(SA_ERR_SHAPE, "n_cols must be a multiple of 8 in [8, 65536]");
+  {
+    // the kernel reads x while other waves write codes and scales: the three must be disjoint
+    const size_t xb = static_cast<size_t>(n_rows) * n_cols * 2, cb = static_cast<size_t>(n_rows) * n_cols,
+                 sb = static_cast<size_t>(n_rows) * sizeof(float);
+    if (overlaps(codes, cb, x, xb) || overlaps(scales, sb, x, xb) || overlaps(codes, cb, scales, sb))
+      return fail(SA_ERR_RANGE, "x, codes and scales must not overlap one another");
+  }
   const hipError_t e = sa::launch_quantize_rows(x, codes, scales, op, n_rows, n_cols, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return ok();
@@ -814,3 +849,9 @@ sa_status sa_cache_counts(const sa_cache* c, int64_t* n_appended, int32_t* n_res
 }
 
 }  // extern "C"
+
+namespace sa {
+int launch_override(int knob) {
+  return knob >= 0 && knob < kNumKnobs ? g_knobs[knob].load(std::memory_order_relaxed) : 0;
+}
+}  // namespace sa

@@ -107,6 +107,10 @@ hipError_t launch_append(const RopeArgs& rope, const CacheGeom& g, const void* k
 hipError_t launch_read(const CacheGeom& g, int store_slot, void* k_out, void* v_out, int dtype,
                        hipStream_t stream);
 
+// Launch-shape overrides set through sa_set_launch_override (0 = automatic).
+enum Knob : int { kKnobAttnWaves = 0, kKnobAttnSplits = 1, kKnobProjTile = 2, kNumKnobs = 3 };
+int launch_override(int knob);
+
 // Waves per workgroup and number of key splits the attention launch uses.
 int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus);
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus);

@@ -52,10 +52,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 constexpr int kSliceBytes = 64;
 constexpr int kGWaves = 4;  // waves per workgroup, a 2 x 2 grid of wave tiles
 constexpr int kOPad = 8;    // epilogue tile row padding (bf16 elements)
-#ifndef PROJ_PRE
-#define PROJ_PRE 3
-#endif
-constexpr int kPre = PROJ_PRE;  // reduction slices in flight in registers
+constexpr int kPre = 3;     // reduction slices in flight in registers
 
 // LDS stage: rows of one 64-byte slice = 4 chunks of 16 bytes, chunk (r, c) stored at
 // r*4 + (c ^ swz(r)).  A 16-byte LDS read is served 16 lanes at a time, and
@@ -577,10 +574,7 @@ int64_t tiles_of(int64_t n_tok, int F, int TM, int TN) { return ((n_tok + TN - 1
 }  // namespace
 
 int proj_tile_shape(int64_t n_tok, int F, int num_cus) {
-  if (const char* e = std::getenv("SA_PROJ_TILE")) {
-    const int v = std::atoi(e);
-    if (v >= 0 && v <= 2) return v;
-  }
+  if (const int v = launch_override(kKnobProjTile)) return v - 1;
   // the largest tile that still gives every CU a workgroup
   if (tiles_of(n_tok, F, 256, 128) >= num_cus) return 0;
   if (tiles_of(n_tok, F, 128, 128) >= num_cus) return 1;

@@ -41,10 +41,11 @@ __device__ __forceinline__ void store8(float* p, const float x[8]) {
   reinterpret_cast<f32x4*>(p)[1] = b;
 }
 
-// One thread rotates 8 channels (4 pairs) of one (stream, token, head).
+// One thread rotates 8 channels (4 pairs) of one (stream, token, head).  It
+// reads its 8 channels before writing the same 8 positions of y, so y may be
+// x itself (no __restrict__: the two may alias).
 template <typename E>
-__global__ void __launch_bounds__(256) rope3d_kernel(RopeArgs rope, const E* __restrict__ x,
-                                                      E* __restrict__ y, int B, int H, int D,
+__global__ void __launch_bounds__(256) rope3d_kernel(RopeArgs rope, const E* x, E* y, int B, int H, int D,
                                                       int T, int n_frames, int64_t t0) {
   const int chunks = D / 8;
   const int64_t total = static_cast<int64_t>(B) * n_frames * T * H * chunks;

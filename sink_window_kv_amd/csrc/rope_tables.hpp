@@ -22,9 +22,11 @@ struct RopeTables {
 
 // t_scale: position interpolation on the time axis (LoL review, PI baseline),
 // folded into the time-axis frequencies: angle t * (w * t_scale).
+// theta: optional per-head, per-axis bases [H][3] given directly (theta_hat
+// itself); theta0, sigma, eps and jitter_axes are then unused.
 inline RopeTables build_rope_tables(int n_heads, int head_dim, const int dims[3], double theta0,
                                     double sigma, const double* eps, uint32_t jitter_axes,
-                                    double t_scale = 1.0) {
+                                    double t_scale = 1.0, const double* theta = nullptr) {
   if (jitter_axes == 0) jitter_axes = 1u;
   if (t_scale == 0.0) t_scale = 1.0;
   RopeTables t;
@@ -34,7 +36,7 @@ inline RopeTables build_rope_tables(int n_heads, int head_dim, const int dims[3]
     double e = eps ? eps[h] : 0.0;
     for (int a = 0; a < 3; ++a) {
       bool jit = (jitter_axes >> a) & 1u;
-      t.theta_hat[h * 3 + a] = jit ? theta0 * (1.0 + sigma * e) : theta0;
+      t.theta_hat[h * 3 + a] = theta ? theta[h * 3 + a] : (jit ? theta0 * (1.0 + sigma * e) : theta0);
     }
     int p = 0;
     for (int a = 0; a < 3; ++a) {
@@ -60,13 +62,16 @@ struct RopeGridTable {
   bool per_head = false;
 };
 
+// One table per head when some head's grid-axis (h or w) base differs from
+// head 0's, else one shared table.
 inline RopeGridTable build_rope_grid_table(const RopeTables& t, int n_heads, int head_dim, const int dims[3],
-                                           int grid_h, int grid_w, uint32_t jitter_axes,
-                                           size_t max_bytes = size_t(32) << 20) {
-  if (jitter_axes == 0) jitter_axes = 1u;
+                                           int grid_h, int grid_w, size_t max_bytes = size_t(32) << 20) {
   RopeGridTable g;
   const int pt = dims[0] / 2, ph = dims[1] / 2, pw = dims[2] / 2;
-  g.per_head = (jitter_axes & 6u) != 0;
+  g.per_head = false;
+  for (int h = 1; h < n_heads; ++h)
+    for (int a = 1; a < 3; ++a)
+      if (t.theta_hat[h * 3 + a] != t.theta_hat[a]) g.per_head = true;
   g.stride = grid_h * ph + grid_w * pw;
   const int n_tab = g.per_head ? n_heads : 1;
   if (static_cast<size_t>(n_tab) * g.stride * 2 * sizeof(float) > max_bytes) {

@@ -49,7 +49,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <cstdlib>
 
 #include "attn_common.hpp"
 
@@ -644,14 +643,11 @@ int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus) {
   (void)D;
   if (dtype == kFP8) return 8;
   if (dtype != kBF16) return 1;
-  if (const char* env = std::getenv("SA_ATTN_WAVES")) {
-    const int v = std::atoi(env);
-    if (v == 4 || v == 8) return v;
-  }
+  if (const int v = launch_override(kKnobAttnWaves)) return v;
   // Eight waves (256 query rows, three K/V stages, one workgroup per CU):
   // half the K/V traffic per query row of the four-wave shape, and measured
   // faster for one stream and for batched multi-frame chunks alike.  Four
-  // waves (two workgroups per CU) stay available through SA_ATTN_WAVES.
+  // waves (two workgroups per CU) stay available as a launch override.
   (void)B; (void)H; (void)T; (void)n_q; (void)num_cus;
   return 8;
 }
@@ -665,10 +661,7 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
   int64_t max_s = key_tiles / 8;  // at least 8 key tiles per split
   if (max_s > 16) max_s = 16;
   if (max_s < 1) max_s = 1;
-  if (const char* env = std::getenv("SA_ATTN_SPLITS")) {
-    const int v = std::atoi(env);
-    if (v >= 1) return static_cast<int>(v < max_s ? v : max_s);
-  }
+  if (const int v = launch_override(kKnobAttnSplits)) return static_cast<int>(v < max_s ? v : max_s);
   // Pick the split count whose workgroup count best fills whole rounds of
   // the CUs' workgroup slots, with a small charge per split for the partial
   // results it writes and merges.

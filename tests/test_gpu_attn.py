@@ -4,9 +4,6 @@ bf16: rel-L2 <= 5e-3 and max-abs <= 2e-2; fp32: <= 1e-5.  At the Wan-1.3B
 shapes the oracle evaluates sampled query rows (every frame's first/last
 rows, tile edges, the ragged tail and random rows) over the full key set.
 """
-import contextlib
-import os
-
 import numpy as np
 import pytest
 
@@ -15,7 +12,7 @@ from oracle import attention as oattn
 from oracle import cache as ocache
 from oracle import rope as orope
 from oracle import stream as ostream
-from swk_testutil import assert_close, log, sample_rows, to_dev, to_np, torch_dtype
+from swk_testutil import assert_close, launch_override, log, sample_rows, to_dev, to_np, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -25,36 +22,20 @@ def _swk():
     return swk
 
 
-@contextlib.contextmanager
-def _env(**kv):
-    """Set launch-shape overrides (SA_ATTN_SPLITS, SA_ATTN_WAVES) for the block; None leaves one unset."""
-    old = {k: os.environ.get(k) for k in kv}
-    for k, v in kv.items():
-        if v is None:
-            os.environ.pop(k, None)
-        else:
-            os.environ[k] = v
-    try:
-        yield
-    finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
 class GpuStream:
     """Drives one layer's cache through the C-ABI and mirrors it in the oracle."""
 
-    def __init__(self, w, layer=0, eps=None, with_oracle=True, t_scale=1.0):
+    def __init__(self, w, layer=0, eps=None, with_oracle=True, t_scale=1.0, theta=None):
+        """theta: optional per-head, per-axis bases [H, 3] handed to the library as a table."""
         import torch
         swk = _swk()
         self.w = w
         self.eps = eps
-        self.rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid, w.theta0, w.sigma, eps, t_scale=t_scale)
+        self.rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid, w.theta0, w.sigma, eps, t_scale=t_scale,
+                             theta=theta)
         self.cache = swk.Cache(self.rope, w.batch, w.n_sink, w.n_local, torch_dtype(w.dtype))
-        bases = orope.theta_hat(w.theta0, w.sigma, eps if eps is not None else np.zeros(w.n_heads))
+        bases = np.asarray(theta, dtype=np.float64) if theta is not None else \
+            orope.theta_hat(w.theta0, w.sigma, eps if eps is not None else np.zeros(w.n_heads))
         self.bases = bases
         self.oracle = ostream.StreamOracle(w.n_sink, w.n_local, w.tokens_per_frame, w.grid[1], w.dims,
                                            bases, t_scale=t_scale) if with_oracle else None
@@ -105,7 +86,7 @@ def test_cfg2_wan_layer_stream(splits, waves):
     """Wan-1.3B layer, bf16, 3 sink + 9 local, 40 frames; checks while filling and in steady state."""
     swk = _swk()
     w = wl.WORKLOADS[2]
-    with _env(SA_ATTN_SPLITS=splits, SA_ATTN_WAVES=waves):
+    with launch_override(splits=splits, waves=waves):
         gs = GpuStream(w)
         rows = sample_rows(w.tokens_per_frame, w.tokens_per_frame)
         check = {0, 1, 2, 3, 11, 12, 20, 39} if splits is None and waves is None else {2, 13, 39}
@@ -189,7 +170,7 @@ def test_stores_start_as_nan_bits(grid):
         gs.cache.k_store.view(torch.int16).fill_(-1)   # bf16 bits 0xffff: a NaN
         gs.cache.v_store.view(torch.int16).fill_(-1)
         torch.cuda.synchronize()
-        with _env(SA_ATTN_WAVES=waves):
+        with launch_override(waves=waves):
             for f in range(w.frames):
                 q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
                 gs.append(k, v, 1, f)
@@ -282,7 +263,7 @@ def test_cfg5_chunked_causal_batched(waves):
         v = wl.chunk_qkv(w, f0, w.chunk, layer, wl.TENSOR_V)
         gs.append(k, v, w.chunk, f0)
         if c in ((0, 1, 3, 9) if waves is None else (3, 9)):
-            with _env(SA_ATTN_WAVES=waves):
+            with launch_override(waves=waves):
                 o = gs.attend(q, w.chunk, swk.SA_MASK_FRAME_CAUSAL)
             _check(gs, q, o, True, rows=rows, heads=heads, what=f"cfg5 chunk {c} waves {waves}")
 
@@ -306,7 +287,7 @@ def test_small_shapes_bf16(D, dims, grid, n_sink, n_local, n_q, mask, frames, wa
         k = wl.chunk_qkv(w, f, n_q, 0, wl.TENSOR_K)
         v = wl.chunk_qkv(w, f, n_q, 0, wl.TENSOR_V)
         gs.append(k, v, n_q, 3 * f + 1)
-        with _env(SA_ATTN_WAVES=waves):
+        with launch_override(waves=waves):
             o = gs.attend(q, n_q, mask)
         _check(gs, q, o, mask == 1, what=f"edge D={D} T={T} frame {f} waves {waves}")
         f += n_q
@@ -339,7 +320,7 @@ def test_running_max_raises(waves):
     swk = _swk()
     w = wl.Workload("growing-scores", 54, batch=1, n_heads=3, head_dim=128, dims=(44, 42, 42), grid=(10, 20),
                     n_sink=2, n_local=6, chunk=1, frames=10, dtype="bf16")
-    with _env(SA_ATTN_WAVES=waves):
+    with launch_override(waves=waves):
         gs = GpuStream(w)
         for f in range(w.frames):
             k = wl.frame_qkv(w, f, tensor=wl.TENSOR_K, scale=0.35 * (1.0 + f))

@@ -4,8 +4,8 @@ import pytest
 
 import workloads as wl
 from oracle import diagnostics as odiag
-from swk_testutil import assert_close, log, sample_rows, to_dev, to_np
-from test_gpu_attn import GpuStream, _env, _swk
+from swk_testutil import launch_override, assert_close, log, sample_rows, to_dev, to_np
+from test_gpu_attn import GpuStream, _swk
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def test_sink_mass_small_stream(waves):
     swk = _swk()
     w = SMALL
     gs = GpuStream(w, eps=wl.head_jitter(w))
-    with _env(SA_ATTN_WAVES=waves):
+    with launch_override(waves=waves):
         for f in range(w.frames):
             q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
             gs.append(k, v, 1, f)
@@ -78,7 +78,7 @@ def test_sink_mass_wan_layer(splits, waves):
     gs = GpuStream(w, eps=wl.head_jitter(w))
     T = w.tokens_per_frame
     rows = sample_rows(T, T, n=64, seed=7)
-    with _env(SA_ATTN_SPLITS=splits, SA_ATTN_WAVES=waves):
+    with launch_override(splits=splits, waves=waves):
         for f in range(14):
             gs.append(wl.frame_qkv(w, f, tensor=wl.TENSOR_K), wl.frame_qkv(w, f, tensor=wl.TENSOR_V), 1, f)
             if f in (0, 2, 5, 13):

@@ -10,8 +10,8 @@ import pytest
 
 import workloads as wl
 from oracle import fp8 as ofp8
-from swk_testutil import log, metrics, sample_rows, to_dev, to_np
-from test_gpu_attn import GpuStream, _env, _swk
+from swk_testutil import launch_override, log, metrics, sample_rows, to_dev, to_np
+from test_gpu_attn import GpuStream, _swk
 
 pytestmark = pytest.mark.gpu
 
@@ -203,7 +203,7 @@ def test_fp8_attention_wan_layer(splits):
     swk = _swk()
     w = wl.WORKLOADS[2]
     rows = sample_rows(w.tokens_per_frame, w.tokens_per_frame, n=64, seed=11)
-    with _env(SA_ATTN_SPLITS=splits):
+    with launch_override(splits=splits):
         gs = Fp8Stream(w, k_scale=1.0 / 64, v_scale=1.0 / 64)
         for f in range(14):
             q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))

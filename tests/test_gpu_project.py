@@ -4,8 +4,8 @@ import pytest
 
 import workloads as wl
 from oracle import project as oproject
-from swk_testutil import assert_close, log, sample_rows, to_dev, to_np, torch_dtype
-from test_gpu_attn import GpuStream, _env, _swk
+from swk_testutil import launch_override, assert_close, log, sample_rows, to_dev, to_np, torch_dtype
+from test_gpu_attn import GpuStream, _swk
 from test_gpu_recache import _read_frame
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +25,7 @@ def _project_stream(w, chunks, tile=None, eps=None, check_rows=None, attend=True
     dq, dk, dv = _weights_dev((wq, wk, wv), w.dtype)
     T = w.tokens_per_frame
     f0, t0 = 0, 0
-    with _env(SA_PROJ_TILE=tile):
+    with launch_override(tile=tile):
         for c in chunks:
             x = wl.frame_hidden(w, f0, c)
             q_out = torch.empty((w.batch, c * T, w.n_heads, w.head_dim), dtype=torch_dtype(w.dtype), device="cuda")
@@ -188,7 +188,7 @@ def test_linear(n_rows, fin, fout, dtype):
     tw = to_dev(np.ascontiguousarray(wo.T), dtype)
     for tile in ((None, "0", "1", "2") if dtype == "bf16" else (None,)):
         y = torch.full((n_rows, fout), float("nan"), dtype=torch_dtype(dtype), device="cuda")
-        with _env(SA_PROJ_TILE=tile):
+        with launch_override(tile=tile):
             swk.sa_linear(tx, tw, y, n_rows, fin, fout)
         torch.cuda.synchronize()
         rel, mx = assert_close(to_np(y), ref, dtype, f"linear {n_rows}x{fin}->{fout} tile {tile}")

@@ -12,8 +12,8 @@ import pytest
 import workloads as wl
 from oracle import project as oproject
 from oracle import quant as oquant
-from swk_testutil import assert_close, log, sample_rows, to_dev, to_np, torch_dtype
-from test_gpu_attn import GpuStream, _check, _env, _swk
+from swk_testutil import launch_override, assert_close, log, sample_rows, to_dev, to_np, torch_dtype
+from test_gpu_attn import GpuStream, _check, _swk
 from test_gpu_recache import _read_frame
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +88,7 @@ def _linear_case(n, C, F, qtype, tile, seed):
     cx, sx, dcx, dsx = _quantize(x, qtype)
     cw, sw, dcw, dsw = _quantize(w, qtype)
     y = torch.empty((n, F), dtype=torch.bfloat16, device="cuda")
-    with _env(SA_PROJ_TILE=tile):
+    with launch_override(tile=tile):
         swk.sa_linear_q8(dcx, dsx, dcw, dsw, y, _qcode(qtype), n, C, F)
     torch.cuda.synchronize()
     ref = oquant.linear_q8(cx, sx, cw, sw, qtype)

@@ -62,6 +62,53 @@ def test_rope3d_apply_position_interpolation(cfg, t0, t_scale):
     log(f"  PI {t_scale:.3f} cfg{cfg} t0={t0}: rel_l2 {rel:.2e} max_abs {mx:.2e}")
 
 
+def test_rope_theta_table_arbitrary_per_axis_bases():
+    """theta_hat given as a per-head, per-axis table (LoL review, method steps (4)-(6)) with a different base
+    on every axis of every head: the standalone rotation at large t, then a jittered Wan-1.3B stream (append
+    rotates K with the table, the attention rotates q) on sampled rows, both against the oracle fed the same
+    table."""
+    import torch
+    from test_gpu_attn import GpuStream, _check
+    swk = _swk()
+    w = wl.WORKLOADS[3]
+    bases = np.random.default_rng(21).uniform(300.0, 30000.0, size=(w.n_heads, 3))
+    rope = swk.Rope(w.n_heads, w.head_dim, w.dims, w.grid, theta=bases)
+    x = wl.chunk_qkv(w, 3, 2, tensor=wl.TENSOR_Q, scale=1.0)
+    tx = to_dev(x, "bf16")
+    ty = torch.empty_like(tx)
+    swk.sa_rope3d_apply(rope, tx, ty, 1, 2, 1199)
+    torch.cuda.synchronize()
+    rel, mx = assert_close(to_np(ty), orope.rope3d(x, 1199, w.tokens_per_frame, bases, w.dims, w.grid[1]),
+                           "bf16", "rope theta table")
+    log(f"  rope with a per-axis theta table: rel_l2 {rel:.2e} max_abs {mx:.2e}")
+    gs = GpuStream(w, theta=bases)
+    rows = np.arange(0, w.tokens_per_frame, 37)
+    for f in range(13):
+        q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=None if t == wl.TENSOR_V else 1.0)
+                   for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+        gs.append(k, v, 1, 50 * f)
+        if f in (0, 12):
+            o = gs.attend(q, 1, swk.SA_MASK_FRAME_CAUSAL)
+            _check(gs, q, o, True, rows=rows, what=f"theta table frame {f} (t = {50 * f})")
+
+
+def test_rope3d_apply_rejects_partial_overlap():
+    """y must be x itself or disjoint from it: a shifted y is SA_ERR_RANGE, and nothing is written."""
+    import torch
+    swk = _swk()
+    w = wl.WORKLOADS[1]
+    rope = _rope_for(w)
+    n = w.batch * w.tokens_per_frame * w.n_heads * w.head_dim
+    buf = torch.zeros(2 * n, dtype=torch.float32, device="cuda")
+    x = buf[:n]
+    y = buf[w.head_dim:w.head_dim + n]       # starts inside x
+    with pytest.raises(swk.SinkAttnError) as e:
+        swk.sa_rope3d_apply(rope, x, y, w.batch, 1, 3)
+    assert e.value.status == swk.SA_ERR_RANGE
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(buf)) == 0
+
+
 def test_rope_all_axes_jittered_and_host_tables():
     """Host tables equal the oracle's theta_hat/frequencies; all-axis jitter parity on device."""
     import torch

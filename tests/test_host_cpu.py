@@ -48,6 +48,50 @@ def test_host_rope_tables_match_oracle(sigma, axes, names):
         np.testing.assert_allclose(fr[h], orope.head_frequencies(bases[h], (44, 42, 42)), rtol=1e-14)
 
 
+def test_host_rope_theta_table_path():
+    """A per-head, per-axis theta_hat table given directly: the eps form's own theta_hat gives the same tables,
+    and an arbitrary per-axis table gives the oracle's frequencies (LoL review, method steps (4)-(5))."""
+    swk = _swk()
+    dims = (44, 42, 42)
+    eps = np.random.default_rng(7).uniform(-1, 1, 12)
+    for axes, names in ((1, ("t",)), (7, ("t", "h", "w")), (6, ("h", "w"))):
+        th_eps, fr_eps = swk.sa_rope_tables(12, 128, dims, (30, 52), 10000.0, 0.8, eps, axes)
+        th_tab, fr_tab = swk.sa_rope_tables(12, 128, dims, (30, 52), theta=th_eps)
+        assert th_tab == th_eps and fr_tab == fr_eps
+    # arbitrary bases, every axis and head different (not expressible as theta0 (1 + sigma eps))
+    bases = np.random.default_rng(8).uniform(50.0, 40000.0, size=(12, 3))
+    th, fr = swk.sa_rope_tables(12, 128, dims, (30, 52), theta0=2.0, sigma=5.0, eps=None, jitter_axes=0,
+                                t_scale=0.5, theta=bases)
+    np.testing.assert_array_equal(np.array(th), bases)
+    for h in range(12):
+        ref = orope.head_frequencies(bases[h], dims)
+        ref[:dims[0] // 2] *= 0.5
+        np.testing.assert_allclose(fr[h], ref, rtol=1e-14)
+    got = np.array(swk.sa_rope_phase_coherence(12, 128, dims, (30, 52), [0, 1, 7, 1200], theta=bases))
+    np.testing.assert_allclose(got, odiag.phase_coherence(bases, dims, [0, 1, 7, 1200]), rtol=0, atol=1e-12)
+    for bad in (1.0, 0.5, float("nan"), float("inf")):
+        b = bases.copy()
+        b[5, 2] = bad
+        with pytest.raises(swk.SinkAttnError) as e:
+            swk.sa_rope_tables(12, 128, dims, (30, 52), theta=b)
+        assert e.value.status == swk.SA_ERR_RANGE and "head 5, axis 2" in str(e.value)
+
+
+def test_host_launch_override_validation():
+    """sa_set_launch_override accepts each knob's set (0 = automatic) and rejects the rest."""
+    swk = _swk()
+    L = swk.lib()
+    for knob, good, bad in ((swk.SA_KNOB_ATTN_WAVES, (0, 4, 8), (1, 2, 16, -1)),
+                            (swk.SA_KNOB_ATTN_SPLITS, (0, 1, 3, 16), (-1, 17)),
+                            (swk.SA_KNOB_PROJ_TILE, (0, 1, 2, 3), (-1, 4))):
+        for v in good:
+            assert L.sa_set_launch_override(knob, v) == swk.SA_OK
+        for v in bad:
+            assert L.sa_set_launch_override(knob, v) == swk.SA_ERR_RANGE
+        assert L.sa_set_launch_override(knob, 0) == swk.SA_OK
+    assert L.sa_set_launch_override(3, 0) == swk.SA_ERR_RANGE
+
+
 @pytest.mark.parametrize("sigma,axes,names,dims", [(0.8, 1, ("t",), (44, 42, 42)), (0.0, 1, ("t",), (44, 42, 42)),
                                                    (0.8, 7, ("t", "h", "w"), (22, 22, 20))])
 def test_host_phase_coherence_matches_oracle(sigma, axes, names, dims):
@@ -108,8 +152,10 @@ def test_host_cache_store_bytes_and_null_checks():
     assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 12 * 12 * 1560 * 128 * 2
     d.dtype = 1
     assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 12 * 12 * 1560 * 128 * 4
+    assert swk.lib().sa_cache_bytes(ctypes.byref(d)) == swk.lib().sa_cache_store_bytes(ctypes.byref(d))
     d.n_local = 0
     assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 0
+    assert swk.lib().sa_cache_bytes(ctypes.byref(d)) == 0
     d.n_local, d.n_sink = 60, 5
     assert swk.lib().sa_cache_store_bytes(ctypes.byref(d)) == 0
     h = ctypes.c_void_p()
@@ -119,10 +165,17 @@ def test_host_cache_store_bytes_and_null_checks():
     assert swk.lib().sa_status_str(6) == b"SA_ERR_RANGE"
 
 
-@pytest.fixture(scope="module")
-def plan_harness():
+# The host slot plan is built twice: plainly, and (host code only, g++) with
+# AddressSanitizer, LeakSanitizer and UndefinedBehaviorSanitizer, any report
+# failing the run.
+_SANITIZE = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+@pytest.fixture(scope="module", params=["plain", "sanitized"])
+def plan_harness(request):
     exe = os.path.join(tempfile.mkdtemp(prefix="swk_plan_"), "plan_harness")
-    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror",
+    extra = _SANITIZE if request.param == "sanitized" else []
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror", *extra,
                     "-I", os.path.join(ROOT, "sink_window_kv_amd", "csrc"),
                     os.path.join(ROOT, "tests", "cpp", "plan_harness.cpp"), "-o", exe], check=True)
     return exe
@@ -130,7 +183,11 @@ def plan_harness():
 
 def _run_plan(exe, n_sink, n_local, cmds):
     inp = f"{n_sink} {n_local}\n" + "\n".join(cmds) + "\n"
-    out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:exitcode=23",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1:exitcode=24")
+    r = subprocess.run([exe], input=inp, capture_output=True, text=True, env=env)
+    assert r.returncode == 0, f"plan harness exited {r.returncode}:\n{r.stderr[-2000:]}"
+    out = r.stdout
     rows = []
     for line in out.strip().splitlines():
         parts = line.split()
@@ -173,6 +230,10 @@ def test_host_q8_validation():
     assert L.sa_quantize_rows(P, Q, S1, E4, 4, 60, None) == swk.SA_ERR_SHAPE      # cols % 8
     assert L.sa_quantize_rows(P, Q, S1, E4, -1, 64, None) == swk.SA_ERR_SHAPE
     assert L.sa_quantize_rows(P, Q, S1, I8, 0, 64, None) == swk.SA_OK             # nothing to do
+    assert L.sa_quantize_rows(P, P + 4 * 64, S1, I8, 4, 64, None) == swk.SA_ERR_RANGE   # codes inside x
+    assert L.sa_quantize_rows(P, Q, P + 16, I8, 4, 64, None) == swk.SA_ERR_RANGE        # scales inside x
+    assert L.sa_quantize_rows(P, Q, Q + 128, E4, 4, 64, None) == swk.SA_ERR_RANGE       # scales inside codes
+    assert L.sa_quantize_rows(P, P, S1, I8, 4, 64, None) == swk.SA_ERR_RANGE            # in place
     assert L.sa_linear_q8(P, S1, Q, S2, None, I8, 4, 64, 64, None) == swk.SA_ERR_NULL
     assert L.sa_linear_q8(P, S1, Q, S2, R, 9, 4, 64, 64, None) == swk.SA_ERR_DTYPE
     assert L.sa_linear_q8(P, S1 + 4, Q, S2, R, I8, 4, 64, 64, None) == swk.SA_ERR_ALIGN
