@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (HBM counter calibration)")
     return ap.parse_args()
@@ -100,6 +100,29 @@ def traffic_from_profile(kernel_srcs):
         return None
 
 
+def profile_of_step(kernel_srcs):
+    """Kernel-only durations of the bench step's attention call from the committed kernel-trace summary,
+    with the shader clock and box it was taken on, if it was taken on the current kernel code (else None)."""
+    path = os.path.join(ROOT, "profiles", "attn_bf16_wan13b_kernel_trace.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        vals[k.strip()] = v.strip().split("  ")[0].strip()
+    if vals.get("kernel_code_sha256_16") != code_digest(kernel_srcs):
+        return None
+    try:
+        att, mrg = float(vals["step_attention_kernel_mean_us"]), float(vals["step_merge_kernel_mean_us"])
+        sclk = int(vals["sclk_mhz_under_load"]) if vals.get("sclk_mhz_under_load", "").isdigit() else None
+    except (KeyError, ValueError):
+        return None
+    return {"attention_kernel_us": att, "merge_kernel_us": mrg, "call_us": round(att + mrg, 2),
+            "sclk_mhz": sclk, "box": vals.get("box")}
+
+
 def sclk_under_load(launch, n_calls: int):
     """Shader clock (MHz) that rocm-smi reports while n_calls launches run, or None."""
     import re
@@ -135,11 +158,7 @@ def cpu_baseline(w, budget_s: float):
     from oracle import attention as oattn
     from oracle import cache as ocache
     from oracle import rope as orope
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    cores = _cores()
     T = w.tokens_per_frame
     bases = orope.theta_hat(w.theta0, w.sigma, np.zeros(w.n_heads))
     f0 = 20
@@ -178,6 +197,75 @@ def cpu_baseline(w, budget_s: float):
                       f"1560 queries x {n_keys} keys each), fp64 numpy incl. the RoPE of every key and query frame "
                       f"it used; {dt:.1f} s of oracle time (input drawing excluded)",
             "latent_frames_per_s_per_layer": (heads_done / w.n_heads) / dt}
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_recache_leg(w4):
+    """The fp64 oracle's KV recache of one Wan-1.3B layer cache (x [18720 x 1536] . W_k, W_v, RoPE of the
+    12 frames' keys), the prompt-switch workload; one whole recache, timed once (input drawing excluded)."""
+    import numpy as np
+    import workloads as wl
+    from oracle import recache as orecache
+    from oracle import rope as orope
+    x, wk, wv = wl.recache_inputs(w4)
+    n = w4.n_sink + w4.n_local
+    bases = orope.theta_hat(w4.theta0, w4.sigma, np.zeros(w4.n_heads))
+    t0 = time.perf_counter()
+    orecache.recache(x, wk, wv, w4.n_heads, list(range(18, 18 + n)), w4.tokens_per_frame, bases, w4.dims,
+                     w4.grid[1])
+    dt = time.perf_counter() - t0
+    flops = 2.0 * x.shape[1] * (2 * w4.n_heads * w4.head_dim) * w4.hidden
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "seconds_per_recache": round(dt, 3),
+            "sample": f"one whole recache: x [{x.shape[1]} x {w4.hidden}] . W_k, W_v [{w4.hidden} x "
+                      f"{w4.n_heads * w4.head_dim}] and the RoPE of the {n} frames' keys, fp64 numpy; timed once"}
+
+
+def cpu_chunk_leg(w5, budget_s: float):
+    """The fp64 oracle on one (stream, layer, 3-frame chunk) of the B = 4 chunked workload in steady state
+    (chunk frames 27-29 over sinks 0-2 and local frames 21-29, frame-causal), head by head until the
+    budget; extrapolated to the 4-stream layer chunk and to the 30-layer step (x 4 streams x 30 layers)."""
+    import numpy as np
+    import workloads as wl
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+    from oracle import rope as orope
+    T, H, D = w5.tokens_per_frame, w5.n_heads, w5.head_dim
+    c, f_last = w5.chunk, 29
+    res = ocache.resident_frames(f_last + 1, w5.n_sink, w5.n_local)
+    qframes = list(range(f_last - c + 1, f_last + 1))
+    bases = orope.theta_hat(w5.theta0, w5.sigma, wl.head_jitter(w5, layer=0))
+    one = lambda f, t: wl.normal((1, T, H, D), w5.cfg, 0, 0, f, t, w5.input_scale, w5.dtype)
+    k = {f: one(f, wl.TENSOR_K) for f in res}
+    v = {f: one(f, wl.TENSOR_V) for f in res}
+    q = np.concatenate([one(f, wl.TENSOR_Q) for f in qframes], axis=1)
+    t0 = time.perf_counter()
+    k_rot = [orope.rope3d_frame(k[f], f, bases, w5.dims, w5.grid[1]) for f in res]
+    q_rot = orope.rope3d(q, 0, T, bases, w5.dims, w5.grid[1], t_list=qframes)
+    dt = time.perf_counter() - t0
+    heads = 0
+    while heads < H and dt <= budget_s:
+        t0 = time.perf_counter()
+        oattn.window_attention(q_rot, k_rot, [v[f] for f in res], res, qframes, T, True, heads=[heads])
+        dt += time.perf_counter() - t0
+        heads += 1
+    per_head = sum(attn_flops(T, (len(res) - c + 1 + i) * T, 1, D) for i in range(c))
+    flops = per_head * heads
+    stream_chunk_s = dt * H / heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            "stream_layer_chunk_s": round(stream_chunk_s, 2),
+            "extrapolated_30_layer_step_s": round(stream_chunk_s * w5.batch * 30, 1),
+            "latent_frames_per_s_per_layer": w5.batch * c / (stream_chunk_s * w5.batch),
+            "sample": f"{heads} of {H} heads of one stream's 3-frame chunk (4680 queries over 10/11/12 frames, "
+                      f"frame-causal, sigma 0.8), fp64 numpy incl. the RoPE of the chunk's queries and the resident "
+                      f"keys; {dt:.1f} s; the stream-layer-chunk time is extrapolated x {H}/{heads} heads, the "
+                      f"30-layer step x 4 streams x 30 layers (extrapolated, not run)"}
 
 
 def main():
@@ -273,38 +361,45 @@ def main():
 
     # LoL diagnostic: the same attention call also reporting each row's
     # softmax mass on the sink frames (a second pass over the sink keys).
+    # Cycled over the 8 layer caches (0.92 GB) like the step, so K/V come from HBM.
     mass = torch.empty((1, T, H), dtype=torch.float32, device=dev)
-    c0 = caches[0]
-    for _ in range(3):
-        swk.sa_window_attn_sink_mass(c0, qs[0], o, mass, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+    for i in range(3):
+        swk.sa_window_attn_sink_mass(caches[i], qs[i], o, mass, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
     em0, em1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     em0.record(stream)
-    for _ in range(20):
-        swk.sa_window_attn_sink_mass(c0, qs[0], o, mass, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
+    for i in range(24):
+        swk.sa_window_attn_sink_mass(caches[i % N_LAYERS], qs[i % pool], o, mass, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
     em1.record(stream)
     torch.cuda.synchronize()
-    mass_us = em0.elapsed_time(em1) * 1e3 / 20
+    mass_us = em0.elapsed_time(em1) * 1e3 / 24
 
     # Window-size variants (3, 12 and 24 local frames without sinks; 9 local
     # + 3 sink is the main workload): steady-state attention of one frame.
+    # Each variant cycles enough caches (at least 3) for a working set above 300 MB, so K/V come from HBM.
     windows = {}
     for n_s, n_l in ((0, 3), (0, 12), (0, 24)):
-        cw = swk.Cache(rope, 1, n_s, n_l, bf, device=dev)
-        for f in range(n_s + n_l):
-            swk.sa_cache_append(cw, ks[f % pool], vs[f % pool], 1, f)
-        wsw = torch.zeros(max(swk.sa_window_attn_workspace(cw, 1) // 4, 4), dtype=torch.float32, device=dev)
-        for _ in range(3):
-            swk.sa_window_attn(cw, qs[0], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, wsw)
+        per_cache = 2 * (n_s + n_l) * T * H * D * 2
+        n_c = max(3, -(-300_000_000 // per_cache))
+        cws = [swk.Cache(rope, 1, n_s, n_l, bf, device=dev) for _ in range(n_c)]
+        for ci, cw in enumerate(cws):
+            for f in range(n_s + n_l):
+                swk.sa_cache_append(cw, ks[(f + ci) % pool], vs[(f + ci) % pool], 1, f)
+        wsw = torch.zeros(max(swk.sa_window_attn_workspace(cws[0], 1) // 4, 4), dtype=torch.float32, device=dev)
+        for i in range(n_c):
+            swk.sa_window_attn(cws[i], qs[i % pool], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, wsw)
+        n_w = 8 * n_c if n_c < 8 else 2 * n_c
         ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ew0.record(stream)
-        for _ in range(20):
-            swk.sa_window_attn(cw, qs[0], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, wsw)
+        for i in range(n_w):
+            swk.sa_window_attn(cws[i % n_c], qs[i % pool], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, wsw)
         ew1.record(stream)
         torch.cuda.synchronize()
-        us_w = ew0.elapsed_time(ew1) * 1e3 / 20
+        us_w = ew0.elapsed_time(ew1) * 1e3 / n_w
         fl_w = attn_flops(T, (n_s + n_l) * T, H, D)
-        windows[f"{n_s}+{n_l}"] = {"attention_avg_us": round(us_w, 1), "TFLOPs": round(fl_w / (us_w * 1e-6) / 1e12, 1)}
-        cw.close()
+        windows[f"{n_s}+{n_l}"] = {"attention_avg_us": round(us_w, 1), "TFLOPs": round(fl_w / (us_w * 1e-6) / 1e12, 1),
+                                   "caches_cycled": n_c, "working_set_MB": round(n_c * per_cache / 1e6)}
+        for cw in cws:
+            cw.close()
     windows["3+9"] = {"attention_avg_us": round(att_avg * 1e3, 1), "TFLOPs": round(achieved, 1)}
 
     # Standalone RoPE (Q of one frame, read + write) and the KV recache.
@@ -320,18 +415,24 @@ def main():
     rope_us = e0.elapsed_time(e1) * 1e3 / 50
     rope_bytes = 2 * T * H * D * 2
 
+    # The recache cycles 3 hidden-state inputs (3 x 57.5 MB) and 3 layer caches (3 x 115 MB), so its
+    # operands come from HBM rather than the 256 MB last-level cache.
     w4 = wl.WORKLOADS[4]
+    txs = []
+    for bi in range(3):
+        x, wk, wv = wl.recache_inputs(w4, base=bi)
+        txs.append(torch.from_numpy(x).to(dev, bf).contiguous())
     x, wk, wv = wl.recache_inputs(w4)
-    tx = torch.from_numpy(x).to(dev, bf).contiguous()
+    tx = txs[0]
     twk = torch.from_numpy(np.ascontiguousarray(wk.T)).to(dev, bf).contiguous()
     twv = torch.from_numpy(np.ascontiguousarray(wv.T)).to(dev, bf).contiguous()
     rc = caches[0]
-    for _ in range(3):
-        swk.sa_cache_recache(rc, tx, twk, twv, w4.hidden)
+    for i in range(3):
+        swk.sa_cache_recache(caches[i], txs[i], twk, twv, w4.hidden)
     e0.record(stream)
-    n_rc = 20
-    for _ in range(n_rc):
-        swk.sa_cache_recache(rc, tx, twk, twv, w4.hidden)
+    n_rc = 21
+    for i in range(n_rc):
+        swk.sa_cache_recache(caches[i % 3], txs[i % 3], twk, twv, w4.hidden)
     e1.record(stream)
     torch.cuda.synchronize()
     rc_us = e0.elapsed_time(e1) * 1e3 / n_rc
@@ -526,6 +627,13 @@ def main():
               f"({rc_flops / (rc_q8_us * 1e-6) / 1e12:.0f} TOP/s)", file=sys.stderr, flush=True)
 
     traffic = traffic_from_profile(ATTN_BF16_SOURCES)
+    prof = profile_of_step(ATTN_BF16_SOURCES)
+    if prof is not None:
+        prof["frac_call"] = round(flops / (prof["call_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        prof["frac_attention_kernel"] = round(flops / (prof["attention_kernel_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if prof["sclk_mhz"] and sclk_mhz:
+            # the same call scaled from the profiled box's clock to this run's
+            prof["call_us_at_this_clock"] = round(prof["call_us"] * prof["sclk_mhz"] / sclk_mhz, 2)
     out = {
         "metric": "sink+window attn TFLOP/s & latent frames/s/layer on 1 MI355X; % bf16 MFMA peak",
         "value": round(value, 2),
@@ -554,7 +662,10 @@ def main():
                                                 if sclk_mhz else None),
                      "traffic": traffic, "kernel": "attn_bf16_kernel<128>",
                      "flops_per_launch": flops, "avg_launch_us": round(att_avg * 1e3, 2),
-                     "median_launch_us": round(att_ms[len(att_ms) // 2] * 1e3, 2)},
+                     "median_launch_us": round(att_ms[len(att_ms) // 2] * 1e3, 2),
+                     "launch_note": "avg_launch_us: HIP events on the launch stream around each sa_window_attn "
+                                    "call of the step (attention kernel + split merge)",
+                     "profile": prof},
         "append": {"avg_us": round(app_avg * 1e3, 2), "bytes": append_bytes,
                    "GBps": round(append_bytes / (app_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBPS},
         "window_variants": {"note": "sink+local frames; one 1560-query frame, frame-causal, steady state",
@@ -562,13 +673,13 @@ def main():
         "sink_mass": {"avg_us": round(mass_us, 1),
                       "vs_attention_only": round(mass_us / (att_avg * 1e3), 3),
                       "note": "sa_window_attn_sink_mass: the attention plus each row's softmax mass on the "
-                              "3 sink frames, per head"},
+                              "3 sink frames, per head; cycled over the 8 layer caches"},
         "rope3d_q": {"avg_us": round(rope_us, 2), "bytes": rope_bytes,
                      "GBps": round(rope_bytes / (rope_us * 1e-6) / 1e9, 1)},
         "recache": {"avg_us": round(rc_us, 1), "flops": rc_flops,
                     "TFLOPs": round(rc_flops / (rc_us * 1e-6) / 1e12, 1),
                     "pct_bf16_peak": round(100.0 * rc_flops / (rc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                    "min_bytes": rc_bytes},
+                    "min_bytes": rc_bytes, "note": "3 hidden-state inputs and 3 layer caches cycled"},
         "layer_block": {"workload": "wan13b self-attention block per frame: x [1560 x 1536] -> fused q/k/v "
                                      "projections + RoPE + append, attention over 12 frames, output projection "
                                      "[1560 x 1536] . [1536 x 1536]",
@@ -600,6 +711,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"]["recache"] = cpu_recache_leg(w4)
+        out["cpu_baseline"]["chunked_b4"] = cpu_chunk_leg(w5, args.cpu_seconds / 2)
     print(json.dumps(out), flush=True)
 
 

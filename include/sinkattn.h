@@ -353,13 +353,16 @@ sa_status sa_cache_counts(const sa_cache* cache, int64_t* n_appended, int32_t* n
  * stay within the same tolerances whatever the shape; the parity tests use
  * this to cover every shape the automatic choice can take.  Not synchronised
  * with calls running on other host threads.
- *   SA_KNOB_ATTN_WAVES   waves per bf16 attention workgroup: 4 or 8
+ *   SA_KNOB_ATTN_KERNEL  bf16 attention kernel: 1 = the default one, 2 = the
+ *                        variant whose waves interleave their matrix
+ *                        products and softmax in one instruction stream
+ *                        (both: eight waves of 32 query rows per workgroup)
  *   SA_KNOB_ATTN_SPLITS  key splits of the bf16 / e4m3 attention: 1 .. 16
  *                        (capped at one split per 8 key tiles)
  *   SA_KNOB_PROJ_TILE    projection GEMM tile (features x tokens):
  *                        1 = 256 x 128, 2 = 128 x 128, 3 = 128 x 64
  * SA_ERR_RANGE for an unknown knob or a value outside its set. */
-typedef enum { SA_KNOB_ATTN_WAVES = 0, SA_KNOB_ATTN_SPLITS = 1, SA_KNOB_PROJ_TILE = 2 } sa_knob;
+typedef enum { SA_KNOB_ATTN_KERNEL = 0, SA_KNOB_ATTN_SPLITS = 1, SA_KNOB_PROJ_TILE = 2 } sa_knob;
 sa_status sa_set_launch_override(sa_knob knob, int32_t value);
 
 const char* sa_status_str(sa_status status);

@@ -21,7 +21,7 @@ SA_MASK_NONE, SA_MASK_FRAME_CAUSAL = 0, 1
 SA_AXIS_T, SA_AXIS_H, SA_AXIS_W = 1, 2, 4
 SA_Q_INT8, SA_Q_E4M3 = 0, 1
 SA_MAX_FRAMES = 64
-SA_KNOB_ATTN_WAVES, SA_KNOB_ATTN_SPLITS, SA_KNOB_PROJ_TILE = 0, 1, 2
+SA_KNOB_ATTN_KERNEL, SA_KNOB_ATTN_SPLITS, SA_KNOB_PROJ_TILE = 0, 1, 2
 
 
 class SinkAttnError(RuntimeError):

@@ -248,7 +248,7 @@ const char* sa_last_error(void) { return g_last_error.c_str(); }
 sa_status sa_set_launch_override(sa_knob knob, int32_t value) {
   bool valid = false;
   switch (knob) {
-    case SA_KNOB_ATTN_WAVES: valid = value == 0 || value == 4 || value == 8; break;
+    case SA_KNOB_ATTN_KERNEL: valid = value >= 0 && value <= 2; break;
     case SA_KNOB_ATTN_SPLITS: valid = value >= 0 && value <= 16; break;
     case SA_KNOB_PROJ_TILE: valid = value >= 0 && value <= 3; break;
     default: return fail(SA_ERR_RANGE, "unknown launch knob %d", static_cast<int>(knob));
@@ -742,7 +742,7 @@ sa::AttnArgs attn_args(const sa_cache* c, const void* q, void* o, int32_t n_q, f
   a.n_splits = splits;
   a.ws = static_cast<float*>(workspace);
   a.store_bytes = static_cast<uint32_t>(sa_cache_store_bytes(&c->desc));
-  a.n_waves = sa::attn_waves(c->desc.dtype, c->desc.batch, c->desc.n_heads, c->desc.head_dim,
+  a.variant = sa::attn_kernel_variant(c->desc.dtype, c->desc.batch, c->desc.n_heads, c->desc.head_dim,
                              c->desc.tokens_per_frame, n_q, device_cus());
   a.key_limit = INT32_MAX;
   a.stat_mode = sa::kStatNone;

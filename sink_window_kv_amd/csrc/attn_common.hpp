@@ -85,6 +85,18 @@ __device__ __forceinline__ void dma16(const u32x4 rsrc, uint32_t voff, const voi
                : "memory", "m0");
 }
 
+// The same transfer without a memory clobber: LDS reads of other stages may be
+// scheduled across it (the stage it fills is read only after a later wait and
+// barrier, both of which do clobber memory).
+__device__ __forceinline__ void dma16_nomem(const u32x4 rsrc, uint32_t voff, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_base)));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "m0");
+}
+
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Plain s_barrier: a __syncthreads() fence would also wait for every load in

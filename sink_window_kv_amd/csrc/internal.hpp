@@ -52,7 +52,7 @@ struct AttnArgs {
   int32_t n_splits;   // key splits (1 = no workspace)
   float* ws;          // split partials, see attn_workspace_bytes
   uint32_t store_bytes;  // bytes of each cache store (< 4 GiB)
-  int32_t n_waves;       // waves per workgroup (bf16 kernel)
+  int32_t variant;       // bf16 kernel variant: 1 default, 2 in-wave pipelined
   int32_t key_limit;     // keys at logical index >= key_limit are hidden (INT32_MAX: none)
   // Per-row statistic, stat[(b*Lq + row)*H + h] (fp32):
   //   kStatNone: not written; kStatLse: the row's log2-sum-exp2 of its scaled
@@ -108,11 +108,11 @@ hipError_t launch_read(const CacheGeom& g, int store_slot, void* k_out, void* v_
                        hipStream_t stream);
 
 // Launch-shape overrides set through sa_set_launch_override (0 = automatic).
-enum Knob : int { kKnobAttnWaves = 0, kKnobAttnSplits = 1, kKnobProjTile = 2, kNumKnobs = 3 };
+enum Knob : int { kKnobAttnKernel = 0, kKnobAttnSplits = 1, kKnobProjTile = 2, kNumKnobs = 3 };
 int launch_override(int knob);
 
 // Waves per workgroup and number of key splits the attention launch uses.
-int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus);
+int attn_kernel_variant(int dtype, int B, int H, int D, int T, int n_q, int num_cus);
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus);
 size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits);
 hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream);

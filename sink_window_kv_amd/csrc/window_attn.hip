@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "attn_common.hpp"
 
@@ -361,11 +362,13 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + 16 * (i >> 3) + (i & 7) >= lim) sacc[kb][i] = kNegInf;
     }
-    // sacc holds s - m_use; raise the running max lazily (rare, wave-uniform)
+    // sacc holds s - m_use; raise the running max lazily (rare; the branch is
+    // wave-uniform, the decision per row).  m stays an integer, so p = 2^(s - m)
+    // is rounded exactly as 2^s would be, whatever m a row has reached.
     const float m_use = m_run == kNegInf ? 0.f : m_run;
     const float mx = max_halves(tile_max(sacc)) + m_use;  // the tile's max of s
     if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = mx > m_run + kLazy ? ceilf(mx) : m_run;
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -486,6 +489,509 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
         w.y = cvt_pk_bf16(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
         *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * hh) = w;
       }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined bf16 kernel: eight waves per workgroup, two per SIMD,
+// each owning 32 query rows.  A SIMD overlaps matrix-core and vector work
+// only inside one wave's instruction stream (an MFMA wave and a VALU wave on
+// one SIMD run nearly one after the other), so each wave interleaves its own
+// work: while the products S(t+1) = K(t+1) Q^T run, it exponentiates and
+// packs the scores of tile t; while O^T += V^T(t) P^T(t) runs, it takes the
+// row maxima of S(t+1).  Q, S and O^T all sit in ordinary vector registers;
+// four K/V stages keep two tiles in flight ahead of the one being multiplied.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// QB row blocks of 32 query rows per wave, 8 / QB waves per workgroup (256
+// query rows, one workgroup per CU, four K/V stages).
+template <int D, bool BIG_T, int QB>
+__global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a) {
+  constexpr int kWaves = 8 / QB;
+  constexpr int kRowsW = 32 * QB;                 // query rows per wave
+  constexpr int kQTile = kWaves * kRowsW;         // 256
+  // Four K/V stages, the K tiles of all four in one array and the V^T tiles
+  // in another: every operand read then addresses its stage and block with
+  // the instruction's 16-bit immediate offset from one per-lane register.
+  __shared__ u32x4 kq[4][kKTile * D / 8];
+  __shared__ u32x4 vq[4][D * kKTile / 8];
+  __shared__ int s_slot[kMaxFrames];
+  constexpr int CPR = D / 8;
+  constexpr int KI = kKTile * CPR / 64 / kWaves;  // K DMA instructions per wave per tile
+  constexpr int VI = D * 8 / 64 / kWaves;         // V^T DMA instructions per wave per tile
+  constexpr int NDMA = KI + VI;
+  constexpr int KS = D / 16;                      // k-steps of an S product
+  constexpr uint32_t kStageBytes = kKTile * D * 2;  // one stage of K, or of V^T
+  static_assert(NDMA <= 8, "one transfer per k-step slot");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const CacheGeom& g = a.g;
+  const int T = g.T;
+  const int Lq = a.n_q * T;
+  const int n_qt = (Lq + kQTile - 1) / kQTile;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = lid % n_qt;
+  const int split = (lid / n_qt) % a.n_splits;
+  const int bh = lid / (n_qt * a.n_splits);
+  const int b = bh / g.H;
+  const int h = bh - b * g.H;
+  const int n_res = a.frames.n;
+  const int first_q = n_res - a.n_q;
+  const int n_keys = n_res * T;
+  if (threadIdx.x < kMaxFrames) s_slot[threadIdx.x] = threadIdx.x < n_res ? a.frames.store_slot[threadIdx.x] : 0;
+
+  const int klim = min(n_keys, a.key_limit);
+  int row[QB], kend[QB];
+  bool row_ok[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    row[qb] = qt * kQTile + wave * kRowsW + 32 * qb + n;
+    row_ok[qb] = row[qb] < Lq;
+    const int qf = row_ok[qb] ? row[qb] / T : a.n_q - 1;
+    kend[qb] = min(a.causal ? (first_q + qf + 1) * T : n_keys, klim);
+  }
+  const int wave_row0 = qt * kQTile + wave_u * kRowsW;
+  const int wave_kmin = min(a.causal ? (first_q + min(wave_row0, Lq - 1) / T + 1) * T : n_keys, klim);
+  const int last_row = min(qt * kQTile + kQTile - 1, Lq - 1);
+  const int kend_wg = min(a.causal ? (first_q + last_row / T + 1) * T : n_keys, klim);
+  const int n_tiles = (kend_wg + kKTile - 1) / kKTile;
+  const int tile_lo = static_cast<int>((static_cast<int64_t>(n_tiles) * split) / a.n_splits);
+  const int tile_hi = static_cast<int>((static_cast<int64_t>(n_tiles) * (split + 1)) / a.n_splits);
+
+  // ---- Q fragments (rotated, scaled to log2 units, bf16), kept in
+  // accumulation registers
+  mfma_bf16x8 qfrag[QB][KS];
+  {
+    u32x4 qv[QB][KS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qf = row_ok[qb] ? row[qb] / T : a.n_q - 1;
+      const int tok = row_ok[qb] ? row[qb] - qf * T : 0;
+      const int64_t t = a.frames.t[first_q + qf];
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                             ((static_cast<int64_t>(b) * Lq + (row_ok[qb] ? row[qb] : 0)) * g.H + h) * D;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok[qb]) {
+          float x[8];
+          unpack_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hh), x);
+          rope_rotate8(a.rope, h, 2 * s + hh, t, tok / a.rope.grid_w, tok % a.rope.grid_w, x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] *= a.scale_log2;
+          v = pack_bf16x8(x);
+        }
+        qv[qb][s] = v;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qfrag[qb][s] = as_bf16x8(qv[qb][s]);
+  }
+
+  mfma_f32x16 oacc[QB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
+  float m_run[QB], l_run[QB];
+  mfma_f32x16 mseed[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mseed[qb][i] = 0.f;
+  }
+
+  uint32_t kaddr[KS];
+  {
+    const int r = key_perm(n);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kaddr[s] = static_cast<uint32_t>((r * CPR + ((2 * s + hh) ^ kswz<D>(r))) * 16);
+  }
+  // V^T operand addresses as full LDS byte addresses, hidden from constant
+  // folding: the V^T stages start 64 KiB into LDS, past what the 16-bit
+  // immediate offset can reach, so the stage and channel block offsets must
+  // be added to a base register that already holds the array's address.
+  typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+  const uint32_t vq_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(&vq[0][0])));
+  uint32_t vaddr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    vaddr[q] = vq_base + static_cast<uint32_t>((n * 8 + (((q << 1) | hh) ^ vswz(n))) * 16);
+    asm volatile("" : "+v"(vaddr[q]));
+  }
+  // operand reads: K of stage st, 32-key block kb, k-step s; V^T of stage st,
+  // 16-key step q, channel block db
+  auto kread = [&](int st, int kb, int s) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&kq[0][0]) + kaddr[s] +
+                                                     st * kStageBytes + kb * 32 * CPR * 16));
+  };
+  auto vread = [&](int st, int q, int db) {
+    return as_bf16x8(*reinterpret_cast<lds_u32x4*>(
+        static_cast<uintptr_t>(vaddr[q] + st * kStageBytes + db * 32 * 8 * 16)));
+  };
+
+  // ---- global -> LDS transfers (as in attn_bf16_kernel: the waves share each tile)
+  const uint16_t* kst = static_cast<const uint16_t*>(g.k_store);
+  const uint16_t* vst = static_cast<const uint16_t*>(g.v_store);
+  const int64_t head_off = static_cast<int64_t>(b) * g.H + h;
+  const int64_t slot_stride = static_cast<int64_t>(g.B) * g.H;
+  const uint32_t blk_elems = static_cast<uint32_t>(T) * D;
+  const u32x4 krsrc = buffer_rsrc(kst, a.store_bytes);
+  const u32x4 vrsrc = buffer_rsrc(vst, a.store_bytes);
+  __syncthreads();
+  auto blk_bytes = [&](int lf) -> uint32_t {
+    const int slot = __builtin_amdgcn_readfirstlane(s_slot[lf]);
+    return static_cast<uint32_t>((static_cast<int64_t>(slot) * slot_stride + head_off) * blk_elems * 2);
+  };
+  struct TilePlan {
+    uint32_t off[NDMA];
+  };
+  int pl_lf0 = 0, pl_jb = T;
+  uint32_t pl_b0 = 0, pl_b1 = 0;
+  if (BIG_T) {
+    pl_b0 = blk_bytes(0);
+    pl_b1 = blk_bytes(min(1, n_res - 1));
+  }
+  uint32_t klane[KI], vlane[VI];
+#pragma unroll
+  for (int u = 0; u < KI; ++u) {
+    const int P = 64 * (wave_u * KI + u) + lane;
+    const int r = P / CPR, c = (P % CPR) ^ kswz<D>(r);
+    klane[u] = static_cast<uint32_t>(r * (D * 2) + c * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < VI; ++u) {
+    const int P = 64 * (wave_u * VI + u) + lane;
+    const int d = P / 8, c = (P % 8) ^ vswz(d);
+    vlane[u] = static_cast<uint32_t>(d * T * 2 + c * 16);
+  }
+  auto plan_tile = [&](int kt) {
+    TilePlan p;
+    const int j0 = kt * kKTile;
+    uint32_t koff0 = 0, koff1 = 0, voff0 = 0, voff1 = 0;
+    int jb = 0;
+    if (BIG_T) {
+      while (j0 >= pl_jb) {
+        ++pl_lf0;
+        pl_jb += T;
+        pl_b0 = pl_b1;
+        pl_b1 = blk_bytes(min(pl_lf0 + 1, n_res - 1));
+      }
+      const int lf0 = pl_lf0;
+      jb = pl_jb;
+      const uint32_t b0 = pl_b0, b1 = pl_b1;
+      koff0 = b0 - static_cast<uint32_t>(lf0) * blk_elems * 2;
+      koff1 = b1 - static_cast<uint32_t>(jb) * D * 2;
+      voff0 = b0 - static_cast<uint32_t>(lf0) * T * 2;
+      voff1 = b1 - static_cast<uint32_t>(jb) * 2;
+      if (j0 + kKTile <= jb && j0 + kKTile <= kend_wg) {
+        const uint32_t kb = koff0 + static_cast<uint32_t>(j0) * (D * 2);
+        const uint32_t vb = voff0 + static_cast<uint32_t>(j0) * 2;
+#pragma unroll
+        for (int u = 0; u < KI; ++u) p.off[u] = kb + klane[u];
+#pragma unroll
+        for (int u = 0; u < VI; ++u) p.off[KI + u] = vb + vlane[u];
+        return p;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KI; ++u) {
+      const int P = 64 * (wave_u * KI + u) + lane;
+      const int r = P / CPR, c = (P % CPR) ^ kswz<D>(r);
+      int j = j0 + r;
+      if (j >= kend_wg) j = j0;
+      uint32_t off;
+      if (BIG_T) {
+        off = (j < jb ? koff0 : koff1) + static_cast<uint32_t>(j) * (D * 2);
+      } else {
+        const int lf = j / T;
+        off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
+              static_cast<uint32_t>(j - lf * T) * (D * 2);
+      }
+      p.off[u] = off + c * 16;
+    }
+#pragma unroll
+    for (int u = 0; u < VI; ++u) {
+      const int P = 64 * (wave_u * VI + u) + lane;
+      const int d = P / 8, c = (P % 8) ^ vswz(d);
+      int j = j0 + c * 8;
+      if (j >= kend_wg) j = j0;
+      uint32_t off;
+      if (BIG_T) {
+        off = (j < jb ? voff0 : voff1) + static_cast<uint32_t>(d) * T * 2 + static_cast<uint32_t>(j) * 2;
+      } else {
+        const int lf = j / T;
+        off = static_cast<uint32_t>((static_cast<int64_t>(s_slot[lf]) * slot_stride + head_off) * blk_elems * 2) +
+              static_cast<uint32_t>(d) * T * 2 + static_cast<uint32_t>(j - lf * T) * 2;
+      }
+      p.off[KI + u] = off;
+    }
+    return p;
+  };
+  auto fire = [&](const TilePlan& p, int u, int st) {
+    if (u < KI)
+      dma16_nomem(krsrc, p.off[u], &kq[st][64 * (wave_u * KI + u)]);
+    else
+      dma16_nomem(vrsrc, p.off[u], &vq[st][64 * (wave_u * VI + (u - KI))]);
+  };
+
+  // Mask the keys a row does not see (register i holds key j0 + 16(i/8) +
+  // 8hh + i%8), and the row maximum of one row block.
+  auto mask_rows = [&](int j0, mfma_f32x16& x, int qb) {
+    const int lim = kend[qb] - j0 - 8 * hh;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (16 * (i >> 3) + (i & 7) >= lim) x[i] = kNegInf;
+  };
+  auto row_max = [&](const mfma_f32x16& x) {
+    const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+    const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+    const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+    return max_halves(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15])));
+  };
+  // ---- one pipeline step over a block of 32 keys (half a tile), in two
+  // interleaved phases separated by scheduling barriers:
+  //   phase 1: S^T products of the next block (every row block, D/16
+  //            k-steps, K operand reads two steps ahead; the first product
+  //            starts from the masked or plain seed), each k-step slot
+  //            followed by an eighth of this block's softmax (per row block 2
+  //            exp2, 1 pack, 1 row-sum dot) and, at a tile's second block, one
+  //            of the next tile's transfers;
+  //   phase 2: O^T += V^T P^T over this block's two 16-key steps (V^T reads
+  //            two ahead), with the row maxima of the next block between the
+  //            products of the second half.
+  // Blocks a row does not see are computed and masked, so neither phase has a
+  // branch inside; the only data-dependent one is the rare running-max raise.
+  auto phase1 = [&](int kst_, int kbn, mfma_f32x16 (&sn)[QB], const mfma_f32x16 (&sc)[QB], u32x4 (&pk)[QB][2],
+                    const TilePlan* np, int nst, int jn) {
+    mfma_bf16x8 kop[3];
+    kop[0] = kread(kst_, kbn, 0);
+    kop[1] = kread(kst_, kbn, 1);
+    // First k-step: the accumulator starts at -m of the row (scores come out
+    // re-based), or at -inf for the keys the row does not see when the next
+    // block reaches past the wave's first row's last visible key.  Deciding
+    // here, before the interleaved work, leaves no branch inside it.
+    if (jn + 32 > wave_kmin) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        mfma_f32x16 seed = mseed[qb];
+        mask_rows(jn, seed, qb);
+        sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qfrag[qb][0], seed, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qfrag[qb][0], mseed[qb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s < KS) {
+        if (s + 2 < KS) kop[(s + 2) % 3] = kread(kst_, kbn, s + 2);
+        if (s > 0) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s % 3], qfrag[qb][s], sn[qb], 0, 0, 0);
+        }
+      }
+      if (np && s < NDMA) fire(*np, s, nst);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {  // pair s of row block qb: 16-key half s/4, word s%4
+        const int s2 = s >> 2, w = s & 3;
+        const float p0 = __builtin_amdgcn_exp2f(sc[qb][8 * s2 + 2 * w]);
+        const float p1 = __builtin_amdgcn_exp2f(sc[qb][8 * s2 + 2 * w + 1]);
+        pk[qb][s2][w] = cvt_pk_bf16(p0, p1);
+        l_run[qb] = dot2_ones(pk[qb][s2][w], l_run[qb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto phase2 = [&](int vst_, int kb, const u32x4 (&pk)[QB][2], const mfma_f32x16 (&sn)[QB], float (&mx)[QB]) {
+    constexpr int NR = 2 * (D / 32);  // V^T operand reads: (s2, db) = (r / (D/32), r % (D/32))
+    static_assert(NR / 2 + QB <= NR, "a slot for each row block's maximum");
+    mfma_bf16x8 vop[3];
+    vop[0] = vread(vst_, 2 * kb, 0);
+    vop[1] = vread(vst_, 2 * kb + 1 / (D / 32), 1 % (D / 32));
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int s2 = r / (D / 32), db = r % (D / 32);
+      if (r + 2 < NR)
+        vop[(r + 2) % 3] = vread(vst_, 2 * kb + (r + 2) / (D / 32), (r + 2) % (D / 32));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[r % 3], as_bf16x8(pk[qb][s2]), oacc[qb][db], 0, 0, 0);
+      // the next block's scores are complete (and past the MFMA result
+      // hazard) from half way on
+      if (r >= NR / 2 && r < NR / 2 + QB) mx[r - NR / 2] = row_max(sn[r - NR / 2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Lazy raise of the running maxima (per row, to an integer; rare, and
+  // wave-uniform as a branch), then the re-base of the block's scores.
+  // sn holds s - m_use; mxr the block's maxima of s - m_use.
+  auto raise_max = [&](mfma_f32x16 (&sn)[QB], const float (&mxr)[QB]) {
+    float m_use[QB], mx[QB];
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_use[qb] = m_run[qb] == kNegInf ? 0.f : m_run[qb];
+      mx[qb] = mxr[qb] + m_use[qb];
+      up = up || mx[qb] > m_run[qb] + kLazy;
+    }
+    if (__any(up)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = mx[qb] > m_run[qb] + kLazy ? ceilf(mx[qb]) : m_run[qb];
+        const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+        const float m_next = m_new == kNegInf ? 0.f : m_new;
+        const float shift = m_next - m_use[qb];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sn[qb][i] -= shift;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mseed[qb][i] = -m_next;
+      }
+    }
+  };
+
+  // ---- the pipeline, in 32-key blocks; block j is half kb = j % 2 of tile
+  // t = j / 2, and tile t lives in LDS stage (t - tile_lo) % 4.  Step j runs
+  // phase 1 [S(j+1) products | softmax of block j] and phase 2 [PV(j)
+  // products | maxima of S(j+1)], then raises the maxima if needed.  At the
+  // second block of tile t the wave first waits until tile t+1 has landed
+  // (only tile t+2's transfers may still be out) and meets the other waves
+  // at a barrier (all are past tile t-1, so its stage is free); tile t+3's
+  // transfers then go into that stage during phase 1.  Past the end the last
+  // tile is fetched again into a stage nobody reads (which keeps the count
+  // of transfers in flight the same at every wait), and the last step's
+  // next-block products are computed and dropped.
+  const int t_last = tile_hi - 1;
+  mfma_f32x16 sa[QB], sb[QB];
+  u32x4 pk[QB][2];
+  if (tile_lo < tile_hi) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const TilePlan pl = plan_tile(min(tile_lo + k, t_last));
+#pragma unroll
+      for (int u = 0; u < NDMA; ++u) fire(pl, u, k);
+    }
+    wait_vmcnt<2 * NDMA>();
+    barrier();
+    // S of the first block, with nothing to overlap
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const mfma_bf16x8 kop = kread(0, 0, s);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qfrag[qb][s], s == 0 ? mseed[qb] : sa[qb], 0, 0, 0);
+      }
+    }
+    float mx0[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (tile_lo * kKTile + 32 > wave_kmin) mask_rows(tile_lo * kKTile, sa[qb], qb);
+      mx0[qb] = row_max(sa[qb]);
+    }
+    raise_max(sa, mx0);
+  }
+  // step over block (t, KB): stage cur holds tile t, nxt tile t+1, fr receives tile t+3
+  auto step = [&](auto kb_c, int t, mfma_f32x16 (&s_cur)[QB], mfma_f32x16 (&s_nxt)[QB], int cur, int nxt, int fr) {
+    constexpr int KB = decltype(kb_c)::value;
+    const int jn = t * kKTile + 32 * KB + 32;  // first key of the next block
+    float mx[QB];
+    if constexpr (KB == 0) {
+      phase1(cur, 1, s_nxt, s_cur, pk, nullptr, 0, jn);
+      phase2(cur, 0, pk, s_nxt, mx);
+      raise_max(s_nxt, mx);
+    } else {
+      wait_vmcnt<NDMA>();
+      barrier();
+      const TilePlan np = plan_tile(min(t + 3, t_last));
+      phase1(nxt, 0, s_nxt, s_cur, pk, &np, fr, jn);
+      phase2(cur, 1, pk, s_nxt, mx);
+      if (t < t_last) raise_max(s_nxt, mx);
+    }
+  };
+  using KB0 = std::integral_constant<int, 0>;
+  using KB1 = std::integral_constant<int, 1>;
+  for (int kt = tile_lo; kt < tile_hi; kt += 4) {
+    step(KB0{}, kt, sa, sb, 0, 1, 3);
+    step(KB1{}, kt, sb, sa, 0, 1, 3);
+    if (kt + 1 < tile_hi) {
+      step(KB0{}, kt + 1, sa, sb, 1, 2, 0);
+      step(KB1{}, kt + 1, sb, sa, 1, 2, 0);
+    }
+    if (kt + 2 < tile_hi) {
+      step(KB0{}, kt + 2, sa, sb, 2, 3, 1);
+      step(KB1{}, kt + 2, sb, sa, 2, 3, 1);
+    }
+    if (kt + 3 < tile_hi) {
+      step(KB0{}, kt + 3, sa, sb, 3, 0, 2);
+      step(KB1{}, kt + 3, sb, sa, 3, 0, 2);
+    }
+  }
+  wait_vmcnt0();
+
+  // ---- epilogue: lane holds O^T[d][row] of its row blocks
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    if (a.n_splits > 1) {
+      if (row_ok[qb]) {
+        const int64_t plane = static_cast<int64_t>(g.B) * g.H * Lq;
+        const int64_t prow = static_cast<int64_t>(bh) * Lq + row[qb];
+        float* po = a.ws + (split * plane + prow) * D;
+        if (a.stat_mode != kStatMass) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x4 w = {oacc[qb][db][4 * gq], oacc[qb][db][4 * gq + 1], oacc[qb][db][4 * gq + 2],
+                               oacc[qb][db][4 * gq + 3]};
+              *reinterpret_cast<f32x4*>(po + 32 * db + 8 * gq + 4 * hh) = w;
+            }
+        }
+        if (hh == 0) {
+          float* pml = a.ws + static_cast<int64_t>(a.n_splits) * plane * D + (split * plane + prow) * 2;
+          pml[0] = m_run[qb];
+          pml[1] = l_tot;
+        }
+      }
+      continue;
+    }
+    if (row_ok[qb] && a.stat_mode != kStatNone && hh == 0)
+      write_stat(a.stat_mode, a.stat + (static_cast<int64_t>(b) * Lq + row[qb]) * g.H + h, m_run[qb], l_tot);
+    if (row_ok[qb] && a.stat_mode != kStatMass) {
+      const float inv = 1.f / l_tot;
+      uint16_t* orow = static_cast<uint16_t*>(a.o) + ((static_cast<int64_t>(b) * Lq + row[qb]) * g.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          uint2 w;
+          w.x = cvt_pk_bf16(oacc[qb][db][4 * gq] * inv, oacc[qb][db][4 * gq + 1] * inv);
+          w.y = cvt_pk_bf16(oacc[qb][db][4 * gq + 2] * inv, oacc[qb][db][4 * gq + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * hh) = w;
+        }
+    }
   }
 }
 
@@ -639,23 +1145,21 @@ __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int attn_waves(int dtype, int B, int H, int D, int T, int n_q, int num_cus) {
-  (void)D;
-  if (dtype == kFP8) return 8;
-  if (dtype != kBF16) return 1;
-  if (const int v = launch_override(kKnobAttnWaves)) return v;
-  // Eight waves (256 query rows, three K/V stages, one workgroup per CU):
-  // half the K/V traffic per query row of the four-wave shape, and measured
-  // faster for one stream and for batched multi-frame chunks alike.  Four
-  // waves (two workgroups per CU) stay available as a launch override.
-  (void)B; (void)H; (void)T; (void)n_q; (void)num_cus;
-  return 8;
+int attn_kernel_variant(int dtype, int B, int H, int D, int T, int n_q, int num_cus) {
+  (void)B; (void)H; (void)D; (void)T; (void)n_q; (void)num_cus;
+  if (dtype != kBF16) return 0;
+  if (const int v = launch_override(kKnobAttnKernel)) return v;
+  // 1: attn_bf16_kernel.  2: attn_bf16_pipe_kernel, the in-wave interleaved
+  // variant; it measures a few per cent slower on the Wan-1.3B layer (its
+  // vector and scalar instruction count per key tile is the larger), so it is
+  // not the default.  Both run eight waves of 32 query rows, one workgroup of
+  // 256 rows per CU.
+  return 1;
 }
 
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus) {
   if (dtype != kBF16 && dtype != kFP8) return 1;
-  const int W = attn_waves(dtype, B, H, D, T, n_q, num_cus);
-  const int64_t q_tile = 32LL * W;
+  const int64_t q_tile = 256;  // query rows per workgroup (every bf16 and e4m3 shape)
   const int64_t tiles = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(n_q) * T + q_tile - 1) / q_tile);
   const int64_t key_tiles = (static_cast<int64_t>(n_res) * T + kKTile - 1) / kKTile;
   int64_t max_s = key_tiles / 8;  // at least 8 key tiles per split
@@ -665,7 +1169,7 @@ int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, i
   // Pick the split count whose workgroup count best fills whole rounds of
   // the CUs' workgroup slots, with a small charge per split for the partial
   // results it writes and merges.
-  const double slots = static_cast<double>(num_cus) * (W == 4 ? 2 : 1);
+  const double slots = static_cast<double>(num_cus);  // one workgroup per CU
   int best = 1;
   double best_score = -1.0;
   for (int64_t s = 1; s <= max_s; ++s) {
@@ -701,19 +1205,20 @@ hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) 
                          a.g.B, a.g.H, Lq, a.n_splits, a.stat_mode, a.stat);
     }
   } else if (dtype == kBF16) {
-    const int W = a.n_waves;
-    const int64_t wgs = static_cast<int64_t>((Lq + 32 * W - 1) / (32 * W)) * BH * a.n_splits;
+    const int64_t wgs = static_cast<int64_t>((Lq + 255) / 256) * BH * a.n_splits;  // 256 query rows per workgroup
     const dim3 grid(static_cast<unsigned>(wgs));
-    const dim3 block(64 * W);
+    const dim3 block(512);
     const bool big_t = a.g.T >= kKTile;
 #define SA_LAUNCH_ATTN(DD, BT, WW) hipLaunchKernelGGL((attn_bf16_kernel<DD, BT, WW>), grid, block, 0, stream, a)
-    if (W == 8) {
+#define SA_LAUNCH_PIPE(DD, BT) hipLaunchKernelGGL((attn_bf16_pipe_kernel<DD, BT, 1>), grid, block, 0, stream, a)
+    if (a.variant != 2) {
       if (a.g.D == 128) { if (big_t) SA_LAUNCH_ATTN(128, true, 8); else SA_LAUNCH_ATTN(128, false, 8); }
       else { if (big_t) SA_LAUNCH_ATTN(64, true, 8); else SA_LAUNCH_ATTN(64, false, 8); }
     } else {
-      if (a.g.D == 128) { if (big_t) SA_LAUNCH_ATTN(128, true, 4); else SA_LAUNCH_ATTN(128, false, 4); }
-      else { if (big_t) SA_LAUNCH_ATTN(64, true, 4); else SA_LAUNCH_ATTN(64, false, 4); }
+      if (a.g.D == 128) { if (big_t) SA_LAUNCH_PIPE(128, true); else SA_LAUNCH_PIPE(128, false); }
+      else { if (big_t) SA_LAUNCH_PIPE(64, true); else SA_LAUNCH_PIPE(64, false); }
     }
+#undef SA_LAUNCH_PIPE
 #undef SA_LAUNCH_ATTN
     if (a.n_splits > 1) {
       const hipError_t e = hipGetLastError();

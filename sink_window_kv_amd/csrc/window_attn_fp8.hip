@@ -267,10 +267,11 @@ __global__ void __launch_bounds__(512, 1) attn_fp8_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
           if (16 * kb + i >= lim) sacc[kb][i] = kNegInf;
     }
+    // lazy, per-row raise of an integer running max (as in the bf16 kernel)
     const float m_use = m_run == kNegInf ? 0.f : m_run;
     const float mx = max_halves(tile_max(sacc)) + m_use;
     if (__any(mx > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = mx > m_run + 8.f ? ceilf(mx) : m_run;
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       lacc[0] *= alpha;

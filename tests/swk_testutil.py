@@ -62,17 +62,18 @@ def sample_rows(L: int, T: int, n: int = 160, seed: int = 0):
     return np.array(sorted(rows))
 
 
-_KNOBS = {"waves": 0, "splits": 1, "tile": 2}
+_KNOBS = {"kernel": 0, "splits": 1, "tile": 2}
 
 
 @contextlib.contextmanager
-def launch_override(waves=None, splits=None, tile=None):
-    """Force attention waves / key splits / projection tile (sa_set_launch_override) for the block.
+def launch_override(kernel=None, splits=None, tile=None):
+    """Force the bf16 attention kernel variant / key splits / projection tile (sa_set_launch_override)
+    for the block.
 
     None leaves a knob automatic; tile counts from 0 (256 x 128, 128 x 128, 128 x 64).
     """
     import sink_window_kv_amd as swk
-    vals = {"waves": waves, "splits": splits, "tile": None if tile is None else int(tile) + 1}
+    vals = {"kernel": kernel, "splits": splits, "tile": None if tile is None else int(tile) + 1}
     for k, v in vals.items():
         swk.sa_set_launch_override(_KNOBS[k], 0 if v is None else int(v))
     try:

@@ -42,14 +42,14 @@ SMALL = wl.Workload("mass-small", 51, batch=2, n_heads=4, head_dim=128, dims=(44
                     n_sink=2, n_local=3, chunk=1, frames=8, dtype="bf16", sigma=0.8)
 
 
-@pytest.mark.parametrize("waves", ["4", "8"])
-def test_sink_mass_small_stream(waves):
+@pytest.mark.parametrize("kernel", ["1", "2"])
+def test_sink_mass_small_stream(kernel):
     """Every frame from the first (query frames that are sinks: mass 1) through eviction; both masks;
     unscaled N(0,1) queries and keys so the softmax is sharp and the mass varies."""
     swk = _swk()
     w = SMALL
     gs = GpuStream(w, eps=wl.head_jitter(w))
-    with launch_override(waves=waves):
+    with launch_override(kernel=kernel):
         for f in range(w.frames):
             q, k, v = (wl.frame_qkv(w, f, tensor=t, scale=1.0) for t in (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
             gs.append(k, v, 1, f)
@@ -69,8 +69,8 @@ def test_sink_mass_chunks_b2():
         _check_mass(gs, q, 3, swk.SA_MASK_FRAME_CAUSAL, what=f"chunk at {f0}")
 
 
-@pytest.mark.parametrize("splits,waves", [(None, None), ("1", None), ("5", None), (None, "4")])
-def test_sink_mass_wan_layer(splits, waves):
+@pytest.mark.parametrize("splits,kernel", [(None, None), ("1", None), ("5", None), (None, "2")])
+def test_sink_mass_wan_layer(splits, kernel):
     """Wan-1.3B layer in steady state (3 sinks + 9 local, 18720 keys), sampled rows, all heads,
     LoL jitter sigma = 0.8; launch shapes forced as for the attention."""
     swk = _swk()
@@ -78,7 +78,7 @@ def test_sink_mass_wan_layer(splits, waves):
     gs = GpuStream(w, eps=wl.head_jitter(w))
     T = w.tokens_per_frame
     rows = sample_rows(T, T, n=64, seed=7)
-    with launch_override(splits=splits, waves=waves):
+    with launch_override(splits=splits, kernel=kernel):
         for f in range(14):
             gs.append(wl.frame_qkv(w, f, tensor=wl.TENSOR_K), wl.frame_qkv(w, f, tensor=wl.TENSOR_V), 1, f)
             if f in (0, 2, 5, 13):

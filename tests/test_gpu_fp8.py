@@ -1,9 +1,13 @@
 """GPU parity of the e4m3 (FP8) cache: stored codes vs the oracle's rounding, attention vs the fp64 oracle.
 
-Two references for the attention:
+Three references for the attention:
 * the exact oracle on the bf16 inputs, at the FP8 tolerance below;
 * the oracle with the cache's K and V replaced by their e4m3-rounded values (oracle/fp8.py), at a
-  tighter tolerance: what remains is q and p at e4m3 precision and the bf16 output.
+  tighter tolerance: what remains is q and p at e4m3 precision and the bf16 output;
+* the e4m3 rounding model of tests/kernel_rounding.py (the oracle's exact rotated queries rounded as the
+  kernel rounds them, the stored codes read back, p rounded to e4m3 along the kernel's tiles, integer
+  running max and key splits): within one bf16 ulp per element.  This is the check that can tell a
+  dropped key tile or a mis-weighted split from rounding (tests/test_kernel_rounding_cpu.py).
 """
 import numpy as np
 import pytest
@@ -21,10 +25,21 @@ pytestmark = pytest.mark.gpu
 # 1/sqrt(effective keys), so the relative error stays near the per-element
 # RMS whatever the window.  Four roundings reach the output against the
 # exact oracle (K and V in the cache, q and p in the kernel): rel-L2 bound
-# 2^-3.  Two against the oracle with e4m3 K and V (q and p): bound 2^-4.
-# Max-abs bounds for V ~ N(0, 1): 0.6 and 0.3.
-FP8_REL, FP8_ABS = 2.0 ** -3, 0.6
-FP8Q_REL, FP8Q_ABS = 2.0 ** -4, 0.3
+# 2^-3.  Two against the oracle with e4m3 K and V (q and p): bound 2^-4
+# (measured 3.5e-2 - 3.9e-2 on the Wan-1.3B layer, above the 2^-5 first
+# tried; a float32 emulation of the kernel gives the same 3.8e-2).  Max-abs
+# bounds: 0.75 and 0.5 of the output's RMS over the compared elements (the
+# emulation's largest element errors are 0.24 and 0.16 of it), plus 2^-3 and
+# 2^-4 of the element's own reference value: where one key dominates a row,
+# the element is large and its rounding errors scale with it rather than with
+# the RMS (a 6-frame stream of 40-token frames showed an element at 4.8 RMS
+# off the exact value by 0.88 RMS, 18 % of itself).
+FP8_REL, FP8_ABS_RMS, FP8_ABS_SELF = 2.0 ** -3, 0.75, 2.0 ** -3
+FP8Q_REL, FP8Q_ABS_RMS, FP8Q_ABS_SELF = 2.0 ** -4, 0.5, 2.0 ** -4
+
+
+def _rms(x):
+    return float(np.sqrt(np.mean(np.square(x))))
 
 
 class Fp8Stream(GpuStream):
@@ -61,7 +76,40 @@ class Fp8Stream(GpuStream):
         return o
 
 
+def _model_fp8(gs, q, causal, rows):
+    """The e4m3 kernel's arithmetic (tests/kernel_rounding.py) on these rows: (o, near-tie allowance), each
+    [B, n_rows, H, D]."""
+    import kernel_rounding as kr
+    from test_gpu_attn import _rotated_queries
+    swk = _swk()
+    w = gs.w
+    T, D = w.tokens_per_frame, w.head_dim
+    n_q = q.shape[1] // T
+    Lq = n_q * T
+    res = gs.oracle.resident()
+    n_res, first_q = len(res), len(res) - n_q
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    qrot = _rotated_queries(gs, q)[:, rows]
+    codes = [_read_codes(gs, i) for i in range(n_res)]
+    K8 = np.concatenate([ofp8.decode(k) for k, _ in codes], axis=1)
+    V8 = np.concatenate([ofp8.decode(v) for _, v in codes], axis=1)
+    nbytes = swk.sa_window_attn_workspace(gs.cache, n_q)
+    splits = max(1, nbytes // (w.batch * w.n_heads * Lq * (D + 2) * 4))
+    last = np.minimum((rows // 256) * 256 + 255, Lq - 1)
+    fend_row = first_q + rows // T + 1 if causal else np.full(rows.size, n_res)
+    fend_wg = first_q + last // T + 1 if causal else np.full(rows.size, n_res)
+    qmul = float(np.float32(np.float32(kr.scale_log2(0.0, D)) * np.float32(gs.ks)))
+    out = np.empty((w.batch, rows.size, w.n_heads, D))
+    extra = np.empty_like(out)
+    for b in range(w.batch):
+        for h in range(w.n_heads):
+            out[b, :, h], extra[b, :, h] = kr.e4m3_attention(qrot[b, :, h], K8[b, :, h], V8[b, :, h], T, fend_row,
+                                                             fend_wg, splits, qmul, gs.vs)
+    return out, extra
+
+
 def _check_fp8(gs, q, o, causal, rows=None, what=""):
+    import kernel_rounding as kr
     got = to_np(o)
     if rows is not None:
         got = got[:, rows]
@@ -69,10 +117,17 @@ def _check_fp8(gs, q, o, causal, rows=None, what=""):
     qref = gs.qoracle.attend(q, causal=causal, rows=rows)
     rel, mx = metrics(got, ref)
     qrel, qmx = metrics(got, qref)
-    log(f"  {what}: vs exact rel_l2 {rel:.2e} max_abs {mx:.2e} | vs e4m3 K/V rel_l2 {qrel:.2e} max_abs {qmx:.2e}")
+    rms = _rms(ref)
+    model, extra = _model_fp8(gs, q, causal, rows)
+    m_rel, eq = kr.assert_matches_model(np.moveaxis(got, 2, 1), np.moveaxis(model, 2, 1), what,
+                                        np.moveaxis(extra, 2, 1))
+    log(f"  {what}: vs exact rel_l2 {rel:.2e} max_abs {mx / rms:.2f} rms | vs e4m3 K/V rel_l2 {qrel:.2e} "
+        f"max_abs {qmx / rms:.2f} rms | vs rounding model rel_l2 {m_rel:.2e}, {eq:.1%} bit-equal")
     assert np.isfinite(got).all(), what
-    assert rel <= FP8_REL and mx <= FP8_ABS, f"{what}: vs exact rel {rel:.3e} max {mx:.3e}"
-    assert qrel <= FP8Q_REL and qmx <= FP8Q_ABS, f"{what}: vs e4m3 K/V rel {qrel:.3e} max {qmx:.3e}"
+    over = np.max(np.abs(got - ref) - (FP8_ABS_RMS * rms + FP8_ABS_SELF * np.abs(ref)))
+    qover = np.max(np.abs(got - qref) - (FP8Q_ABS_RMS * rms + FP8Q_ABS_SELF * np.abs(qref)))
+    assert rel <= FP8_REL and over <= 0.0, f"{what}: vs exact rel {rel:.3e} max {mx:.3e} (rms {rms:.3e})"
+    assert qrel <= FP8Q_REL and qover <= 0.0, f"{what}: vs e4m3 K/V rel {qrel:.3e} max {qmx:.3e} (rms {rms:.3e})"
 
 
 def _read_codes(gs, idx):
@@ -259,9 +314,10 @@ def test_fp8_project_append_and_recache():
         swk.sa_window_attn(gs.cache, q_out, o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws)
         torch.cuda.synchronize()
         got = to_np(o)
-        rel, mx = metrics(got, gs.oracle.attend(q_ref, causal=True))
-        log(f"  projected fp8 frame {f}: attention vs exact rel_l2 {rel:.2e} max_abs {mx:.2e}")
-        assert rel <= FP8_REL and mx <= FP8_ABS
+        ref = gs.oracle.attend(q_ref, causal=True)
+        rel, mx = metrics(got, ref)
+        log(f"  projected fp8 frame {f}: attention vs exact rel_l2 {rel:.2e} max_abs {mx / _rms(ref):.2f} rms")
+        assert rel <= FP8_REL and np.max(np.abs(got - ref) - (FP8_ABS_RMS * _rms(ref) + FP8_ABS_SELF * np.abs(ref))) <= 0
     # recache with fresh weights
     res = gs.oracle.resident()
     x, wk2, wv2 = wl.recache_inputs(w, n_frames=len(res))
