@@ -312,6 +312,21 @@ sa_status sa_window_attn_workspace(const sa_cache* cache, int32_t n_q, size_t* b
 sa_status sa_window_attn(const sa_cache* cache, const void* q, void* o, int32_t n_q, float scale,
                          sa_mask mask, void* workspace, size_t workspace_bytes, void* stream);
 
+/* sa_window_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments, checks and results as sa_window_attn, with
+ * the key-split partials kept in a 32 MiB scratch array the library holds on
+ * each GPU (from the GPU's first use until the process ends); no workspace
+ * argument, and no allocation of any kind.  SA_ERR_RANGE when this call's
+ * partials exceed 32 MiB (sa_window_attn_workspace() gives the size; the
+ * Wan-1.3B frame of 1560 queries over 12 frames needs 29.2 MB).  Every call
+ * on one GPU shares that GPU's scratch, which keeps the last call's contents
+ * (each call writes what it reads, so nothing needs clearing): calls that
+ * overlap in time on one GPU -- on different streams, or from different host
+ * threads -- race and give wrong results. */
+sa_status sa_window_attn_noalloc(const sa_cache* cache, const void* q, void* o, int32_t n_q, float scale,
+                                 sa_mask mask, void* stream);
+
 /* LoL collapse diagnostic ([LoL] "core method" paragraph: at a sink collapse
  * several heads at once put abnormally high attention weight on the sink
  * frames).  Same arguments, workspace and output o as sa_window_attn, plus

@@ -88,6 +88,7 @@ _SIGNATURES = {
     "sa_window_attn_workspace": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "sa_window_attn": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _VP,
                                       ctypes.c_size_t, _VP]),
+    "sa_window_attn_noalloc": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _VP]),
     "sa_cache_slots": (ctypes.c_int, [_VP, ctypes.POINTER(sa_slot), ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32)]),
     "sa_cache_read": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP, _VP]),
@@ -337,6 +338,13 @@ def sa_window_attn(cache: Cache, q, o, n_q: int, scale: float = 0.0, mask: int =
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().sa_window_attn(cache.handle, _ptr(q), _ptr(o), n_q, scale, mask, _ptr(workspace),
                                 ws_bytes, _stream(stream)), "sa_window_attn")
+
+
+def sa_window_attn_noalloc(cache: Cache, q, o, n_q: int, scale: float = 0.0, mask: int = SA_MASK_NONE,
+                           stream=None):
+    """sa_window_attn with the key-split partials in the library's own device scratch (no workspace)."""
+    _check(lib().sa_window_attn_noalloc(cache.handle, _ptr(q), _ptr(o), n_q, scale, mask, _stream(stream)),
+           "sa_window_attn_noalloc")
 
 
 def sa_window_attn_sink_mass(cache: Cache, q, o, sink_mass, n_q: int, scale: float = 0.0,

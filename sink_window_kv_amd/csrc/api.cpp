@@ -763,6 +763,27 @@ sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q,
   return ok();
 }
 
+sa_status sa_window_attn_noalloc(const sa_cache* c, const void* q, void* o, int32_t n_q, float scale, sa_mask mask,
+                                 void* stream) {
+  if (!c || !q || !o) return fail(SA_ERR_NULL, "cache, q and o must be non-NULL");
+  int splits = 1;
+  size_t need = 0;
+  if (sa_status s = attn_plan(c, n_q, &splits, &need)) return s;
+  if (need > sa::kNoAllocScratchBytes)
+    return fail(SA_ERR_RANGE, "this call needs %zu bytes of key-split scratch; the library holds %zu "
+                "(use sa_window_attn with a workspace)", need, sa::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = sa::attn_noalloc_scratch(&scratch);
+    if (e != hipSuccess || !scratch) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+  }
+  if (sa_status s = check_attn(c, q, o, n_q, scale, mask, scratch, need)) return s;
+  const sa::AttnArgs a = attn_args(c, q, o, n_q, scale, mask, scratch);
+  const hipError_t e = sa::launch_window_attn(a, c->desc.dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
 sa_status sa_window_attn_sink_mass(const sa_cache* c, const void* q, void* o, float* sink_mass, int32_t n_q,
                                    float scale, sa_mask mask, void* workspace, size_t workspace_bytes,
                                    void* stream) {

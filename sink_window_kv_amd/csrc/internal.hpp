@@ -115,6 +115,10 @@ int launch_override(int knob);
 int attn_kernel_variant(int dtype, int B, int H, int D, int T, int n_q, int num_cus);
 int attn_num_splits(int dtype, int B, int H, int D, int T, int n_q, int n_res, int num_cus);
 size_t attn_workspace_bytes(int dtype, int B, int H, int D, int T, int n_q, int n_splits);
+// The library's own attention scratch on the current device (sa_window_attn_noalloc):
+// kNoAllocScratchBytes at *ptr, resolved once per device; allocates nothing.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t attn_noalloc_scratch(void** ptr);
 hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream);
 // The e4m3 attention kernel alone (head_dim 128); launch_window_attn adds the split merge.
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream);

@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -1143,7 +1144,33 @@ __global__ void __launch_bounds__(kF32Rows) attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// Device-resident scratch of sa_window_attn_noalloc: the key-split partials,
+// for callers that cannot allocate.  In host code this name is only a
+// stand-in for the device array; its device address, which differs per GPU,
+// comes from hipGetSymbolAddress and is kept in g_scratch_ptr.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
 }  // namespace
+
+hipError_t attn_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // once per device, with that device current
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
 
 int attn_kernel_variant(int dtype, int B, int H, int D, int T, int n_q, int num_cus) {
   (void)B; (void)H; (void)D; (void)T; (void)n_q; (void)num_cus;
