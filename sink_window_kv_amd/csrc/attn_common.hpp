@@ -104,17 +104,5 @@ __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)
 // across it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Map the hardware workgroup id to a logical one so that each XCD (workgroups
-// are dealt round-robin to the 8 XCDs) gets a contiguous range of logical
-// ids: the q-tiles of one (stream, head, split) then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int pid, int n) {
-  constexpr int X = 8;
-  const int xcd = pid % X;
-  const int local = pid / X;
-  const int per = (n + X - 1) / X;
-  const int tall = n % X == 0 ? X : n % X;
-  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
-}
-
 }  // namespace
 }  // namespace sa

@@ -109,4 +109,17 @@ __device__ __forceinline__ void rope_rotate8(const RopeArgs& r, int h, int chunk
   }
 }
 
+// Map the hardware workgroup id to a logical one so that each XCD (workgroups
+// are dealt round-robin to the 8 XCDs) gets a contiguous range of logical
+// ids: neighbouring logical workgroups, which a kernel arranges to share
+// operand tiles, then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  constexpr int X = 8;
+  const int xcd = pid % X;
+  const int local = pid / X;
+  const int per = (n + X - 1) / X;
+  const int tall = n % X == 0 ? X : n % X;
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 }  // namespace sa

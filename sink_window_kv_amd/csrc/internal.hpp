@@ -91,6 +91,7 @@ struct ProjArgs {
   int32_t op;                  // ProjOp of x and the weights (the output is bf16 unless op and dtype are fp32)
   const float* x_scale;        // [n_tok], 8-bit operands only
   const float* w_scale[3];     // [width] per segment, 8-bit operands only (16-byte aligned)
+  int32_t xcd_order;           // set by the launcher: workgroup order contiguous per XCD (small grids)
   // Cache outputs only: token n is token tok of frame j of stream b, with
   // n = (b * frames.n + j) * T + tok.
   CacheGeom g;
