@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the shader-clock sample (rocm-smi, a child process): for runs under a counter "
+                         "profiler, whose preloaded library has initialised the GPU in every child")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (HBM counter calibration)")
@@ -347,8 +350,9 @@ def main():
 
     # Shader clock under this load: about a second of attention calls queued,
     # rocm-smi read once while they run (null if the tool is not there).
-    sclk_mhz = sclk_under_load(lambda i: swk.sa_window_attn(caches[i % N_LAYERS], qs[i % pool], o, 1, 0.0,
-                                                             swk.SA_MASK_FRAME_CAUSAL, ws), n_calls=6000)
+    sclk_mhz = None if args.no_sclk else sclk_under_load(
+        lambda i: swk.sa_window_attn(caches[i % N_LAYERS], qs[i % pool], o, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL, ws),
+        n_calls=6000)
 
     flops = attn_flops(T, n_win * T, H, D)
     ms_per_step = elapsed * 1e3 / args.steps

@@ -28,7 +28,11 @@
  *   before anything is changed or launched: on error the handle is left as it
  *   was and sa_last_error() (thread-local) describes the problem.
  *   SA_ERR_HIP reports a HIP runtime / launch error; device faults surface at
- *   the caller's next synchronisation.
+ *   the caller's next synchronisation -- or, with SA_DEBUG_SYNC=1 in the
+ *   environment when the library loads, at the call that caused them: every
+ *   entry point then waits for its stream after launching and returns
+ *   SA_ERR_HIP naming the launch (debugging only; it serialises the stream
+ *   and must not be used under HIP graph capture).
  * - Handles are not thread-safe; distinct handles are independent.  A handle
  *   is bound to the device that was current at its creation.
  * - Alignment: every device pointer must be 16-byte aligned.

@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -71,6 +72,26 @@ size_t elem_size(sa_dtype d) { return d == SA_FP8 ? 1 : (d == SA_BF16 ? 2 : 4); 
 
 sa_status hip_fail(hipError_t e, const char* what) {
   return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// SA_DEBUG_SYNC=1 in the environment (read once, when the library loads):
+// every entry point waits for its stream after launching, so a device fault
+// is reported by the call that caused it instead of at the caller's next
+// synchronisation.  For debugging only: it serialises the stream, and a call
+// under HIP graph capture must not synchronise.
+const bool g_debug_sync = [] {
+  const char* v = std::getenv("SA_DEBUG_SYNC");
+  return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}();
+
+// Status of a launch just made on stream (e: the launch's own error).
+sa_status launched(hipError_t e, void* stream, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (g_debug_sync) {
+    const hipError_t es = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (es != hipSuccess) return fail(SA_ERR_HIP, "%s (SA_DEBUG_SYNC): %s", what, hipGetErrorString(es));
+  }
+  return SA_OK;
 }
 
 sa_status check_rope_desc(const sa_rope_desc* d) {
@@ -352,7 +373,7 @@ sa_status sa_rope3d_apply(const sa_rope* rope, const void* x, void* y, sa_dtype 
   const hipError_t e = sa::launch_rope3d(rope_args(rope), x, y, dtype, batch, rope->n_heads,
                                          rope->head_dim, T, n_frames, t0,
                                          static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "rope3d launch");
+  if (sa_status s_ = launched(e, stream, "rope3d launch")) return s_;
   return ok();
 }
 
@@ -422,7 +443,7 @@ sa_status sa_cache_append(sa_cache* c, const void* k, const void* v, int32_t n_f
   const sa::FrameTable chunk = chunk_table(c, n_frames, t0);
   const hipError_t e = sa::launch_append(rope_args(c->rope), geom(c), k, v, c->desc.dtype, chunk,
                                          static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  if (sa_status s_ = launched(e, stream, "append launch")) return s_;
   c->plan.commit_append(n_frames, t0);
   return ok();
 }
@@ -445,7 +466,7 @@ sa_status sa_cache_recache(sa_cache* c, const void* x, const void* w_k, const vo
   a.n_tok = n_tok;
   a.frames = resident_table(c);
   const hipError_t e = sa::launch_proj(a, proj_dtype(c), device_cus(), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "recache launch");
+  if (sa_status s_ = launched(e, stream, "recache launch")) return s_;
   return ok();
 }
 
@@ -474,7 +495,7 @@ sa_status sa_cache_project_append(sa_cache* c, const void* x, const void* w_q, c
   a.n_tok = n_tok;
   a.frames = chunk_table(c, n_frames, t0);
   const hipError_t e = sa::launch_proj(a, proj_dtype(c), device_cus(), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  if (sa_status s_ = launched(e, stream, "projection launch")) return s_;
   c->plan.commit_append(n_frames, t0);
   return ok();
 }
@@ -501,7 +522,7 @@ sa_status sa_linear(const void* x, const void* w, void* y, sa_dtype dtype, int64
   a.n_seg = 1;
   for (int i = 0; i < 3; ++i) a.seg[i] = sa::ProjSeg{w, y, sa::kOutRows};
   const hipError_t e = sa::launch_proj(a, dtype, device_cus(), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  if (sa_status s_ = launched(e, stream, "linear launch")) return s_;
   return ok();
 }
 
@@ -537,7 +558,7 @@ sa_status sa_quantize_rows(const void* x, void* codes, float* scales, sa_qtype q
       return fail(SA_ERR_RANGE, "x, codes and scales must not overlap one another");
   }
   const hipError_t e = sa::launch_quantize_rows(x, codes, scales, op, n_rows, n_cols, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  if (sa_status s_ = launched(e, stream, "quantize launch")) return s_;
   return ok();
 }
 
@@ -573,7 +594,7 @@ sa_status sa_linear_q8(const void* x_codes, const float* x_scales, const void* w
   a.op = op;
   a.x_scale = x_scales;
   const hipError_t e = sa::launch_proj(a, sa::kBF16, device_cus(), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  if (sa_status s_ = launched(e, stream, "linear launch")) return s_;
   return ok();
 }
 
@@ -614,7 +635,7 @@ sa_status sa_cache_recache_q8(sa_cache* c, const void* x_codes, const float* x_s
   a.n_tok = n_tok;
   a.frames = resident_table(c);
   const hipError_t e = sa::launch_proj(a, sa::kBF16, device_cus(), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "recache launch");
+  if (sa_status s_ = launched(e, stream, "recache launch")) return s_;
   return ok();
 }
 
@@ -663,7 +684,7 @@ sa_status sa_cache_project_append_q8(sa_cache* c, const void* x_codes, const flo
   a.n_tok = n_tok;
   a.frames = chunk_table(c, n_frames, t0);
   const hipError_t e = sa::launch_proj(a, sa::kBF16, device_cus(), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  if (sa_status s_ = launched(e, stream, "projection launch")) return s_;
   c->plan.commit_append(n_frames, t0);
   return ok();
 }
@@ -759,7 +780,7 @@ sa_status sa_window_attn(const sa_cache* c, const void* q, void* o, int32_t n_q,
   if (sa_status s = check_attn(c, q, o, n_q, scale, mask, workspace, workspace_bytes)) return s;
   const sa::AttnArgs a = attn_args(c, q, o, n_q, scale, mask, workspace);
   const hipError_t e = sa::launch_window_attn(a, c->desc.dtype, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (sa_status s_ = launched(e, stream, "attention launch")) return s_;
   return ok();
 }
 
@@ -780,7 +801,7 @@ sa_status sa_window_attn_noalloc(const sa_cache* c, const void* q, void* o, int3
   if (sa_status s = check_attn(c, q, o, n_q, scale, mask, scratch, need)) return s;
   const sa::AttnArgs a = attn_args(c, q, o, n_q, scale, mask, scratch);
   const hipError_t e = sa::launch_window_attn(a, c->desc.dtype, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (sa_status s_ = launched(e, stream, "attention launch")) return s_;
   return ok();
 }
 
@@ -813,7 +834,7 @@ sa_status sa_window_attn_sink_mass(const sa_cache* c, const void* q, void* o, fl
   a.stat_mode = n_sink_res > 0 ? sa::kStatLse : sa::kStatZero;
   a.stat = sink_mass;
   hipError_t e = sa::launch_window_attn(a, c->desc.dtype, st);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (sa_status s_ = launched(e, stream, "attention launch")) return s_;
   if (n_sink_res > 0) {
     // pass 2: the same rows over the sink keys only (the first n_sink_res
     // resident frames); the mass is 2^(LSE_sink - LSE_all).  At most as many
@@ -827,7 +848,7 @@ sa_status sa_window_attn_sink_mass(const sa_cache* c, const void* q, void* o, fl
     a.o = nullptr;
     a.stat_mode = sa::kStatMass;
     e = sa::launch_window_attn(a, c->desc.dtype, st);
-    if (e != hipSuccess) return hip_fail(e, "sink-mass launch");
+    if (sa_status s_ = launched(e, st, "sink-mass launch")) return s_;
   }
   return ok();
 }
@@ -858,7 +879,7 @@ sa_status sa_cache_read(const sa_cache* c, int32_t index, void* k_out, void* v_o
     return fail(SA_ERR_RANGE, "k_out and v_out must not overlap the cache stores");
   const hipError_t e = sa::launch_read(geom(c), res[index].store_slot, k_out, v_out, c->desc.dtype,
                                        static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "read launch");
+  if (sa_status s_ = launched(e, stream, "read launch")) return s_;
   return ok();
 }
 
