@@ -379,7 +379,8 @@ sa_status sa_cache_counts(const sa_cache* cache, int64_t* n_appended, int32_t* n
  *   SA_KNOB_ATTN_SPLITS  key splits of the bf16 / e4m3 attention: 1 .. 16
  *                        (capped at one split per 8 key tiles)
  *   SA_KNOB_PROJ_TILE    projection GEMM tile (features x tokens):
- *                        1 = 256 x 128, 2 = 128 x 128, 3 = 128 x 64
+ *                        1 = 256 x 128, 2 = 128 x 128, 3 = 128 x 64,
+ *                        4 = 256 x 256 (eight waves, one workgroup per CU)
  * SA_ERR_RANGE for an unknown knob or a value outside its set. */
 typedef enum { SA_KNOB_ATTN_KERNEL = 0, SA_KNOB_ATTN_SPLITS = 1, SA_KNOB_PROJ_TILE = 2 } sa_knob;
 sa_status sa_set_launch_override(sa_knob knob, int32_t value);

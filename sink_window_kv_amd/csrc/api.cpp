@@ -271,7 +271,7 @@ sa_status sa_set_launch_override(sa_knob knob, int32_t value) {
   switch (knob) {
     case SA_KNOB_ATTN_KERNEL: valid = value >= 0 && value <= 2; break;
     case SA_KNOB_ATTN_SPLITS: valid = value >= 0 && value <= 16; break;
-    case SA_KNOB_PROJ_TILE: valid = value >= 0 && value <= 3; break;
+    case SA_KNOB_PROJ_TILE: valid = value >= 0 && value <= 4; break;
     default: return fail(SA_ERR_RANGE, "unknown launch knob %d", static_cast<int>(knob));
   }
   if (!valid) return fail(SA_ERR_RANGE, "value %d is outside the set of knob %d", value, static_cast<int>(knob));

@@ -50,7 +50,16 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // A reduction slice is 64 bytes of every operand row: 32 bf16 or 64 8-bit codes.
 constexpr int kSliceBytes = 64;
-constexpr int kGWaves = 4;  // waves per workgroup, a 2 x 2 grid of wave tiles
+// Waves per workgroup: a 2 x WN grid of wave tiles of (TM/2) x (TN/WN), each
+// (TM/64) x (TN/(32 WN)) products of 32 x 32.  Four waves (two workgroups per
+// CU) for the smaller tiles; eight waves and one workgroup per CU for the
+// 256 x 256 tile, whose slices carry 1.5 times the products per byte staged.
+template <int TM, int TN>
+struct GemmShape {
+  static constexpr int NW = (TM == 256 && TN == 256) ? 8 : 4;
+  static constexpr int WN = NW / 2;
+  static constexpr int WG_PER_CU = NW == 8 ? 1 : 2;
+};
 constexpr int kOPad = 8;    // epilogue tile row padding (bf16 elements)
 constexpr int kPre = 3;     // reduction slices in flight in registers
 
@@ -112,24 +121,26 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
   constexpr int EB = QT == kOpBF16 ? 2 : 1;    // operand bytes per element
   constexpr int TKE = kSliceBytes / EB;        // reduction elements per slice
   using Acc = typename std::conditional<QT == kOpI8, i32x16, mfma_f32x16>::type;
+  constexpr int NW = GemmShape<TM, TN>::NW;    // waves per workgroup
+  constexpr int WN = GemmShape<TM, TN>::WN;    // wave columns (tokens)
   constexpr int MI = TM / 64;                  // 32-row products per wave (features)
-  constexpr int NJ = TN / 64;                  // 32-column products per wave (tokens)
-  constexpr int kAI = TM * 4 / (kGWaves * 64); // feature-tile transfers per wave per slice
-  constexpr int kBI = TN * 4 / (kGWaves * 64); // token-tile transfers per wave per slice
-  static_assert(kAI * kGWaves * 64 == TM * 4 && kBI * kGWaves * 64 == TN * 4, "whole tiles");
+  constexpr int NJ = TN / (32 * WN);           // 32-column products per wave (tokens)
+  constexpr int kAI = TM * 4 / (NW * 64);      // feature-tile transfers per wave per slice
+  constexpr int kBI = TN * 4 / (NW * 64);      // token-tile transfers per wave per slice
+  static_assert(kAI * NW * 64 == TM * 4 && kBI * NW * 64 == TN * 4, "whole tiles");
   __shared__ GemmSmem<TM, TN> sm;
   GemmStage<TM, TN>* stg = sm.stg;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int C = a.hidden;
   const int width = a.width;
   const int F = a.n_seg * width;
   const int64_t n_tok = a.n_tok;
-  // Workgroup order: token tiles vary fastest.  On a small grid (a few
-  // workgroups per CU: the per-frame projections) each XCD takes a
+  // Workgroup order: token tiles vary fastest.  On a small grid (at most two
+  // rounds of workgroups: the per-frame projections) each XCD takes a
   // contiguous range of that order, so the workgroups it runs at once share
   // one feature tile of W and neighbouring x tiles in its L2 (measured 7 -
   // 11 % faster there); on the recache's large grid the hardware's
@@ -180,7 +191,7 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
 #pragma unroll
   for (int i = 0; i < MI; ++i) arow[i] = wm * (TM / 2) + 32 * i + n;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) brow[j] = wn * (TN / 2) + 32 * j + n;
+  for (int j = 0; j < NJ; ++j) brow[j] = wn * (TN / WN) + 32 * j + n;
 
   Acc acc[MI][NJ];
 #pragma unroll
@@ -223,7 +234,7 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
   __shared__ int64_t s_t[TN], s_kb[TN], s_vb[TN];
   if (a.has_key || a.has_value) {
     const int per_stream = a.frames.n * g.T;
-    for (int t = threadIdx.x; t < TN; t += kGWaves * 64) {
+    for (int t = threadIdx.x; t < TN; t += NW * 64) {
       const int64_t tkn = n0 + t;
       int row = 0, col = 0;
       int64_t tt = 0, kb = 0, vb = 0;
@@ -273,7 +284,7 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
       tcs_t0 = time_of(n0);
       const int64_t t1 = time_of(min(n0 + TN, n_tok) - 1);
       const int pt = a.rope.pairs_t;
-      for (int i = threadIdx.x; i < 2 * tcs_nh * pt; i += kGWaves * 64) {
+      for (int i = threadIdx.x; i < 2 * tcs_nh * pt; i += NW * 64) {
         const int fi = i / (tcs_nh * pt), rem = i - fi * tcs_nh * pt;
         const int hh2 = rem / pt, pp = rem - hh2 * pt;
         float sn, cs;
@@ -366,21 +377,27 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
   }
 
   // Epilogue.  acc[i][j][r]: feature m0 + wm*TM/2 + 32i + 8(r/4) + 4hh + r%4,
-  // token n0 + wn*TN/2 + 32j + n.  Key features are rotated at their token's
+  // token n0 + wn*TN/WN + 32j + n.  Key features are rotated at their token's
   // position (4 consecutive features = 2 pairs in-lane), everything is
   // rounded to bf16 into the LDS tile, then written out in 16-byte pieces:
   // row-major and key rows [tok][d] directly, value rows [d][tok] gathered
   // per feature.
   // The segment of feature f: at most three, so two compares.
   auto seg_of = [&](int f) { return (f >= width ? 1 : 0) + (f >= 2 * width ? 1 : 0); };
+  // Per-segment fields as scalars, selected per lane: indexing the argument
+  // array with a lane's segment number would load it from memory each time.
+  const int kind0 = a.seg[0].kind, kind1 = a.seg[1].kind, kind2 = a.seg[2].kind;
+  auto kind_of = [&](int sg) { return sg == 0 ? kind0 : (sg == 1 ? kind1 : kind2); };
   // A tile of value features only (the recache and per-frame projections put
   // the value segment last and tiles are aligned to it when the width is a
   // multiple of the tile): kept transposed in LDS.
   const bool allv = a.has_value && m0 >= (a.n_seg - 1) * width && a.seg[a.n_seg - 1].kind == kOutCacheV;
+  const int pt = a.rope.pairs_t, pth = a.rope.pairs_th;
+  const int ph = pth - pt, pw = a.rope.pairs_all - pth;
   asm volatile("s_barrier" ::: "memory");  // every wave is done with the stages
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int tl = wn * (TN / 2) + 32 * j + n;
+    const int tl = wn * (TN / WN) + 32 * j + n;
     const int64_t tkn = n0 + tl;
     int row = 0, col = 0;
     int64_t t = 0;
@@ -389,6 +406,7 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
       col = s_col[tl];
       t = s_t[tl];
     }
+    const int tsel = t == tcs_t0 ? 0 : 1;
     float sx = 1.f;
     if constexpr (QT != kOpBF16) sx = tkn < n_tok ? a.x_scale[tkn] : 0.f;
 #pragma unroll
@@ -397,37 +415,58 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int fl = wm * (TM / 2) + 32 * i + 8 * q + 4 * hh;
         const int f = m0 + fl;  // multiple of 4
+        const int sg = seg_of(f);
         float v[4] = {static_cast<float>(acc[i][j][4 * q]), static_cast<float>(acc[i][j][4 * q + 1]),
                       static_cast<float>(acc[i][j][4 * q + 2]), static_cast<float>(acc[i][j][4 * q + 3])};
         if constexpr (QT != kOpBF16) {
           // (acc * sx[token]) * sw[feature]; the 4 features lie in one segment
           f32x4 sw = {0.f, 0.f, 0.f, 0.f};
           if (f < F) {
-            const int s = seg_of(f);
-            sw = *reinterpret_cast<const f32x4*>(a.w_scale[s] + (f - s * width));
+            const float* wsc = sg == 0 ? a.w_scale[0] : (sg == 1 ? a.w_scale[1] : a.w_scale[2]);
+            sw = *reinterpret_cast<const f32x4*>(wsc + (f - sg * width));
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = (v[r] * sx) * sw[r];
         }
-        if (a.has_key && f < F) {
-          const int s = seg_of(f);
-          if (a.seg[s].kind == kOutCacheK) {
-            const int fs = f - s * width;
-            const int head = fs >> dshift, d = fs & (g.D - 1);
+        if (a.has_key && f < F && kind_of(sg) == kOutCacheK) {
+          // the lane's 4 features are 2 pairs, p0 and p0 + 1
+          const int fs = f - sg * width;
+          const int head = fs >> dshift, d = fs & (g.D - 1);
+          const int p0 = d / 2;
+          auto rot = [&](int pp, float cs, float sn) {
+            const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
+            v[2 * pp] = x0 * cs - x1 * sn;
+            v[2 * pp + 1] = x0 * sn + x1 * cs;
+          };
+          if (tcs_nh > 0 && p0 + 1 < pt) {
+            // time axis, both pairs: the tile's table
+            const float2* e = &s_tcs[(tsel * tcs_nh + (head - tcs_h0)) * pt + p0];
+            const float2 e0 = e[0];
+            rot(0, e0.x, e0.y);
+            const float2 e1 = e[1];
+            rot(1, e1.x, e1.y);
+          } else if (p0 >= pt && a.rope.grid_cs != nullptr && (p0 + 1 < pth || p0 >= pth)) {
+            // grid axes, both pairs on one axis: neighbouring table entries
+            const int idx = p0 < pth ? row * ph + (p0 - pt) : a.rope.grid_h * ph + col * pw + (p0 - pth);
+            const float2* e = reinterpret_cast<const float2*>(a.rope.grid_cs) +
+                              (a.rope.grid_per_head ? head * a.rope.grid_stride : 0) + idx;
+            const float2 e0 = e[0];
+            rot(0, e0.x, e0.y);
+            const float2 e1 = e[1];
+            rot(1, e1.x, e1.y);
+          } else {
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-              const int p = d / 2 + pp;
+              const int p = p0 + pp;
               float sn, cs;
-              if (tcs_nh > 0 && p < a.rope.pairs_t) {
-                const float2 e = s_tcs[((t == tcs_t0 ? 0 : 1) * tcs_nh + (head - tcs_h0)) * a.rope.pairs_t + p];
+              if (tcs_nh > 0 && p < pt) {
+                const float2 e = s_tcs[(tsel * tcs_nh + (head - tcs_h0)) * pt + p];
                 cs = e.x;
                 sn = e.y;
               } else {
                 rope_cs(a.rope, head, p, t, row, col, &sn, &cs);
               }
-              const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
-              v[2 * pp] = x0 * cs - x1 * sn;
-              v[2 * pp + 1] = x0 * sn + x1 * cs;
+              rot(pp, cs, sn);
             }
           }
         }
@@ -443,70 +482,86 @@ __device__ __forceinline__ void proj_body(ProjArgs a) {
       }
   }
   __syncthreads();
-  uint16_t* kst = static_cast<uint16_t*>(g.k_store);
-  uint16_t* vst = static_cast<uint16_t*>(g.v_store);
-  // 16-byte pieces (token, 8 features): row-major outputs and keys
-  for (int e = allv ? TN * (TM / 8) : threadIdx.x; e < TN * (TM / 8); e += kGWaves * 64) {
-    const int tl = e / (TM / 8), fl = (e % (TM / 8)) * 8;
-    const int64_t tkn = n0 + tl;
+  // Write-out in 16-byte pieces.  A thread's feature column (row-major and
+  // key outputs) or token column (values) is the same for all its pieces, so
+  // everything that depends only on it is resolved once, before its loop.
+  constexpr int kNT = NW * 64;  // threads
+  if (!allv) {
+    // (token, 8 features) pieces: row-major outputs and keys, kNT / (TM/8)
+    // tokens per pass
+    constexpr int kPerTok = TM / 8;
+    const int fl = (threadIdx.x % kPerTok) * 8;
     const int f = m0 + fl;
-    if (tkn >= n_tok || f >= F) continue;
-    const int s = seg_of(f);
-    const int fs = f - s * width;
-    const u32x4 piece = *reinterpret_cast<const u32x4*>(&sm.out.o[tl][fl]);
-    if (a.seg[s].kind == kOutRows) {
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.seg[s].y) + tkn * width + fs) = piece;
-    } else if (a.seg[s].kind == kOutCacheK) {
-      const int head = fs >> dshift, d = fs & (g.D - 1);
-      const int64_t idx = s_kb[tl] + static_cast<int64_t>(head) * g.T * g.D + d;
-      if (a.cache_fp8) {
-        float x[8];
-        unpack_bf16x8(piece, x);
-        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(g.k_store) + idx) = to_e4m3x8(x, 1.f / g.k_scale);
-      } else {
-        *reinterpret_cast<u32x4*>(kst + idx) = piece;
+    if (f < F) {
+      const int sg = seg_of(f);
+      const int fs = f - sg * width;
+      const int kind = kind_of(sg);
+      if (kind == kOutRows) {
+        uint16_t* const ybase = static_cast<uint16_t*>(sg == 0 ? a.seg[0].y : (sg == 1 ? a.seg[1].y : a.seg[2].y)) + fs;
+        for (int tl = threadIdx.x / kPerTok; tl < TN && n0 + tl < n_tok; tl += kNT / kPerTok)
+          *reinterpret_cast<u32x4*>(ybase + (n0 + tl) * width) = *reinterpret_cast<const u32x4*>(&sm.out.o[tl][fl]);
+      } else if (kind == kOutCacheK) {
+        const int64_t hoff = static_cast<int64_t>(fs >> dshift) * g.T * g.D + (fs & (g.D - 1));
+        if (a.cache_fp8) {
+          uint8_t* const kb8 = static_cast<uint8_t*>(g.k_store) + hoff;
+          const float inv = 1.f / g.k_scale;
+          for (int tl = threadIdx.x / kPerTok; tl < TN && n0 + tl < n_tok; tl += kNT / kPerTok) {
+            float x[8];
+            unpack_bf16x8(*reinterpret_cast<const u32x4*>(&sm.out.o[tl][fl]), x);
+            *reinterpret_cast<uint2*>(kb8 + s_kb[tl]) = to_e4m3x8(x, inv);
+          }
+        } else {
+          uint16_t* const kb16 = static_cast<uint16_t*>(g.k_store) + hoff;
+          for (int tl = threadIdx.x / kPerTok; tl < TN && n0 + tl < n_tok; tl += kNT / kPerTok)
+            *reinterpret_cast<u32x4*>(kb16 + s_kb[tl]) = *reinterpret_cast<const u32x4*>(&sm.out.o[tl][fl]);
+        }
       }
     }
   }
   if (!a.has_value) return;
-  // 16-byte pieces (feature, 8 tokens): values
-  for (int e = threadIdx.x; e < TM * (TN / 8); e += kGWaves * 64) {
-    const int fl = e / (TN / 8), tl = (e % (TN / 8)) * 8;
-    const int f = m0 + fl;
-    const int64_t tkn0 = n0 + tl;
-    if (f >= F || tkn0 >= n_tok) continue;
-    const int s = seg_of(f);
-    if (a.seg[s].kind != kOutCacheV) continue;
+  {
+    // (feature, 8 tokens) pieces: values, kNT / (TN/8) features per pass;
     // 8 consecutive tokens stay in one frame and stream (T % 8 == 0)
-    const int fv = f - s * width;
-    const int head = fv >> dshift, d = fv & (g.D - 1);
-    alignas(16) uint16_t vals[8];
-    if (allv) {
-      *reinterpret_cast<u32x4*>(vals) = *reinterpret_cast<const u32x4*>(&sm.out.ot[fl][tl]);
-    } else {
+    constexpr int kPerFeat = TN / 8;
+    const int tl = (threadIdx.x % kPerFeat) * 8;
+    if (n0 + tl < n_tok) {
+      const int64_t vb = s_vb[tl];
+      for (int fl = threadIdx.x / kPerFeat; fl < TM; fl += kNT / kPerFeat) {
+        const int f = m0 + fl;
+        if (f >= F) break;
+        const int sg = seg_of(f);
+        if (kind_of(sg) != kOutCacheV) continue;
+        const int64_t idx = vb + static_cast<int64_t>(f - sg * width) * g.T;  // (head * D + d) * T
+        alignas(16) uint16_t vals[8];
+        if (allv) {
+          *reinterpret_cast<u32x4*>(vals) = *reinterpret_cast<const u32x4*>(&sm.out.ot[fl][tl]);
+        } else {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) vals[r] = sm.out.o[tl + r][fl];
-    }
-    const int64_t idx = s_vb[tl] + static_cast<int64_t>(head * g.D + d) * g.T;
-    if (a.cache_fp8) {
-      float x[8];
+          for (int r = 0; r < 8; ++r) vals[r] = sm.out.o[tl + r][fl];
+        }
+        if (a.cache_fp8) {
+          float x[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) x[r] = bf16_bits_to_f32(vals[r]);
-      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(g.v_store) + idx) = to_e4m3x8(x, 1.f / g.v_scale);
-    } else {
-      *reinterpret_cast<u32x4*>(vst + idx) = *reinterpret_cast<const u32x4*>(vals);
+          for (int r = 0; r < 8; ++r) x[r] = bf16_bits_to_f32(vals[r]);
+          *reinterpret_cast<uint2*>(static_cast<uint8_t*>(g.v_store) + idx) = to_e4m3x8(x, 1.f / g.v_scale);
+        } else {
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(g.v_store) + idx) = *reinterpret_cast<const u32x4*>(vals);
+        }
+      }
     }
   }
 }
 
 template <int TM, int TN>
-__global__ void __launch_bounds__(kGWaves * 64, 2) proj_bf16_kernel(ProjArgs a) {
+__global__ void __launch_bounds__((GemmShape<TM, TN>::NW * 64), (GemmShape<TM, TN>::WG_PER_CU))
+    proj_bf16_kernel(ProjArgs a) {
   proj_body<TM, TN, kOpBF16>(a);
 }
 
 // 8-bit operands (QT = kOpE4M3 or kOpI8), bf16 results.
 template <int TM, int TN, int QT>
-__global__ void __launch_bounds__(kGWaves * 64, 2) proj_q8_kernel(ProjArgs a) {
+__global__ void __launch_bounds__((GemmShape<TM, TN>::NW * 64), (GemmShape<TM, TN>::WG_PER_CU))
+    proj_q8_kernel(ProjArgs a) {
   proj_body<TM, TN, QT>(a);
 }
 
@@ -574,15 +629,15 @@ void launch_tile(const ProjArgs& a0, int num_cus, hipStream_t stream) {
   const int F = a0.n_seg * a0.width;
   const int64_t n_tt = (a0.n_tok + TN - 1) / TN, n_ft = (F + TM - 1) / TM;
   ProjArgs a = a0;
-  a.xcd_order = n_tt * n_ft <= 4 * static_cast<int64_t>(num_cus);
+  a.xcd_order = n_tt * n_ft <= 2 * GemmShape<TM, TN>::WG_PER_CU * static_cast<int64_t>(num_cus);  // <= 2 rounds
   const dim3 grid = a.xcd_order ? dim3(static_cast<unsigned>(n_tt * n_ft))
                                 : dim3(static_cast<unsigned>(n_tt), static_cast<unsigned>(n_ft));
   if (a.op == kOpE4M3)
-    hipLaunchKernelGGL((proj_q8_kernel<TM, TN, kOpE4M3>), grid, dim3(kGWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((proj_q8_kernel<TM, TN, kOpE4M3>), grid, dim3(GemmShape<TM, TN>::NW * 64), 0, stream, a);
   else if (a.op == kOpI8)
-    hipLaunchKernelGGL((proj_q8_kernel<TM, TN, kOpI8>), grid, dim3(kGWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((proj_q8_kernel<TM, TN, kOpI8>), grid, dim3(GemmShape<TM, TN>::NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((proj_bf16_kernel<TM, TN>), grid, dim3(kGWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((proj_bf16_kernel<TM, TN>), grid, dim3(GemmShape<TM, TN>::NW * 64), 0, stream, a);
 }
 
 int64_t tiles_of(int64_t n_tok, int F, int TM, int TN) { return ((n_tok + TN - 1) / TN) * ((F + TM - 1) / TM); }
@@ -604,6 +659,7 @@ hipError_t launch_proj(const ProjArgs& a, int dtype, int num_cus, hipStream_t st
     switch (proj_tile_shape(a.n_tok, F, num_cus)) {
       case 0: launch_tile<256, 128>(a, num_cus, stream); break;
       case 1: launch_tile<128, 128>(a, num_cus, stream); break;
+      case 3: launch_tile<256, 256>(a, num_cus, stream); break;
       default: launch_tile<128, 64>(a, num_cus, stream); break;
     }
   } else {

@@ -70,7 +70,7 @@ def launch_override(kernel=None, splits=None, tile=None):
     """Force the bf16 attention kernel variant / key splits / projection tile (sa_set_launch_override)
     for the block.
 
-    None leaves a knob automatic; tile counts from 0 (256 x 128, 128 x 128, 128 x 64).
+    None leaves a knob automatic; tile counts from 0 (256 x 128, 128 x 128, 128 x 64, 256 x 256).
     """
     import sink_window_kv_amd as swk
     vals = {"kernel": kernel, "splits": splits, "tile": None if tile is None else int(tile) + 1}

@@ -65,7 +65,7 @@ SMALL = wl.Workload("project-small", 46, batch=2, n_heads=4, head_dim=128, dims=
                     n_sink=2, n_local=3, chunk=1, frames=8, dtype="bf16", sigma=0.8, hidden=256)
 
 
-@pytest.mark.parametrize("tile", [None, "0", "1", "2"])
+@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
 def test_project_append_stream_small(tile):
     """Chunks of 1-3 frames through sinks, ring wrap and eviction; every tile shape of the GEMM."""
     _project_stream(SMALL, [1, 2, 1, 3, 1, 2], tile=tile, eps=wl.head_jitter(SMALL))
@@ -75,7 +75,7 @@ def test_project_append_ragged_d64():
     """head_dim 64, 3 heads (q, k, v segments of 192 features straddle 128/256-feature tiles), hidden 96."""
     w = wl.Workload("project-d64", 47, batch=3, n_heads=3, head_dim=64, dims=(22, 22, 20), grid=(6, 12),
                     n_sink=1, n_local=2, chunk=1, frames=5, dtype="bf16", hidden=96)
-    for tile in ("0", "1", "2"):
+    for tile in ("0", "1", "2", "3"):
         log(f"d64 tile {tile}")
         _project_stream(w, [1, 1, 2, 1], tile=tile)
 
@@ -186,7 +186,7 @@ def test_linear(n_rows, fin, fout, dtype):
     ref = oproject.linear(x, wo)
     tx = to_dev(x, dtype)
     tw = to_dev(np.ascontiguousarray(wo.T), dtype)
-    for tile in ((None, "0", "1", "2") if dtype == "bf16" else (None,)):
+    for tile in ((None, "0", "1", "2", "3") if dtype == "bf16" else (None,)):
         y = torch.full((n_rows, fout), float("nan"), dtype=torch_dtype(dtype), device="cuda")
         with launch_override(tile=tile):
             swk.sa_linear(tx, tw, y, n_rows, fin, fout)

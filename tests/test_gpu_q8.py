@@ -104,7 +104,7 @@ def _linear_case(n, C, F, qtype, tile, seed):
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
-@pytest.mark.parametrize("tile", [None, "0", "1", "2"])
+@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
 def test_linear_q8_output_projection_shape(qtype, tile):
     """One frame's output projection (1560 x 1536 -> 1536) in every tile shape; int8 bit-exact."""
     log(f"linear_q8 {qtype} tile {tile}")

@@ -4,7 +4,7 @@ import pytest
 
 import workloads as wl
 from oracle import recache as orecache
-from swk_testutil import assert_close, log, sample_rows, to_dev, to_np, torch_dtype
+from swk_testutil import launch_override, assert_close, log, sample_rows, to_dev, to_np, torch_dtype
 from test_gpu_attn import GpuStream, _check, _swk
 
 pytestmark = pytest.mark.gpu
@@ -157,8 +157,10 @@ def test_recache_errors():
     # tokens per frame 40 so 128-token tiles cross frames and streams
     (5, 64, (22, 22, 20), (4, 10), 320),
 ])
-def test_recache_bf16_ragged_tiles(n_heads, head_dim, dims, grid, hidden):
-    """bf16 recache where features and tokens do not fill whole GEMM tiles, with a wrapped ring."""
+@pytest.mark.parametrize("tile", [None, "3"])
+def test_recache_bf16_ragged_tiles(n_heads, head_dim, dims, grid, hidden, tile):
+    """bf16 recache where features and tokens do not fill whole GEMM tiles, with a wrapped ring; the automatic
+    tile and the 256 x 256 eight-wave tile."""
     import torch
     swk = _swk()
     w = wl.Workload("recache-ragged", 45, batch=2, n_heads=n_heads, head_dim=head_dim, dims=dims, grid=grid,
@@ -170,8 +172,9 @@ def test_recache_bf16_ragged_tiles(n_heads, head_dim, dims, grid, hidden):
     res = gs.oracle.resident()
     x, wk, wv = wl.recache_inputs(w, n_frames=len(res))
     log(f"recache ragged H={n_heads} D={head_dim} grid={grid} hidden={hidden} resident={res}")
-    swk.sa_cache_recache(gs.cache, to_dev(x, "bf16"), to_dev(np.ascontiguousarray(wk.T), "bf16"),
-                         to_dev(np.ascontiguousarray(wv.T), "bf16"), w.hidden)
+    with launch_override(tile=tile):
+        swk.sa_cache_recache(gs.cache, to_dev(x, "bf16"), to_dev(np.ascontiguousarray(wk.T), "bf16"),
+                             to_dev(np.ascontiguousarray(wv.T), "bf16"), w.hidden)
     torch.cuda.synchronize()
     gs.oracle.recache(x, wk, wv)
     for i, f in enumerate(res):

@@ -83,7 +83,7 @@ def test_host_launch_override_validation():
     L = swk.lib()
     for knob, good, bad in ((swk.SA_KNOB_ATTN_KERNEL, (0, 1, 2), (3, 4, 8, -1)),
                             (swk.SA_KNOB_ATTN_SPLITS, (0, 1, 3, 16), (-1, 17)),
-                            (swk.SA_KNOB_PROJ_TILE, (0, 1, 2, 3), (-1, 4))):
+                            (swk.SA_KNOB_PROJ_TILE, (0, 1, 2, 3, 4), (-1, 5))):
         for v in good:
             assert L.sa_set_launch_override(knob, v) == swk.SA_OK
         for v in bad:
