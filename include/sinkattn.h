@@ -375,7 +375,8 @@ sa_status sa_cache_counts(const sa_cache* cache, int64_t* n_appended, int32_t* n
  *   SA_KNOB_ATTN_KERNEL  bf16 attention kernel: 1 = the default one, 2 = the
  *                        variant whose waves interleave their matrix
  *                        products and softmax in one instruction stream
- *                        (both: eight waves of 32 query rows per workgroup)
+ *                        (both: eight waves of 32 query rows per workgroup),
+ *                        3 = that variant with four waves of 64 rows
  *   SA_KNOB_ATTN_SPLITS  key splits of the bf16 / e4m3 attention: 1 .. 16
  *                        (capped at one split per 8 key tiles)
  *   SA_KNOB_PROJ_TILE    projection GEMM tile (features x tokens):

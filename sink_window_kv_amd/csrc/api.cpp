@@ -269,7 +269,7 @@ const char* sa_last_error(void) { return g_last_error.c_str(); }
 sa_status sa_set_launch_override(sa_knob knob, int32_t value) {
   bool valid = false;
   switch (knob) {
-    case SA_KNOB_ATTN_KERNEL: valid = value >= 0 && value <= 2; break;
+    case SA_KNOB_ATTN_KERNEL: valid = value >= 0 && value <= 3; break;
     case SA_KNOB_ATTN_SPLITS: valid = value >= 0 && value <= 16; break;
     case SA_KNOB_PROJ_TILE: valid = value >= 0 && value <= 4; break;
     default: return fail(SA_ERR_RANGE, "unknown launch knob %d", static_cast<int>(knob));

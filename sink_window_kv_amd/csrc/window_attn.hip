@@ -494,25 +494,30 @@ __global__ void __launch_bounds__(W * 64, 8 / W) attn_bf16_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined bf16 kernel: eight waves per workgroup, two per SIMD,
-// each owning 32 query rows.  A SIMD overlaps matrix-core and vector work
-// only inside one wave's instruction stream (an MFMA wave and a VALU wave on
-// one SIMD run nearly one after the other), so each wave interleaves its own
-// work: while the products S(t+1) = K(t+1) Q^T run, it exponentiates and
-// packs the scores of tile t; while O^T += V^T(t) P^T(t) runs, it takes the
-// row maxima of S(t+1).  Q, S and O^T all sit in ordinary vector registers;
-// four K/V stages keep two tiles in flight ahead of the one being multiplied.
+// Software-pipelined bf16 kernel, in two shapes: eight waves per workgroup
+// (two per SIMD) of 32 query rows each, or four waves (one per SIMD) of 64
+// rows each.  A SIMD overlaps matrix-core and vector work only inside one
+// wave's instruction stream (an MFMA wave and a VALU wave on one SIMD run
+// nearly one after the other), so each wave interleaves its own work: while
+// the products S(t+1) = K(t+1) Q^T run, it exponentiates and packs the scores
+// of tile t; while O^T += V^T(t) P^T(t) runs, it takes the row maxima of
+// S(t+1).  A 64-row wave feeds each K and V^T operand read to two products
+// and runs a tile's addressing, transfers and waits once for both row
+// blocks.  Q and S sit in ordinary vector registers, O^T too in the 32-row
+// shape and in AGPRs in the 64-row one; four K/V stages keep two tiles in
+// flight ahead of the one being multiplied.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// QB row blocks of 32 query rows per wave, 8 / QB waves per workgroup (256
-// query rows, one workgroup per CU, four K/V stages).
+// QB (1 or 2) row blocks of 32 query rows per wave, 8 / QB waves per
+// workgroup (256 query rows, one workgroup per CU, four K/V stages).
 template <int D, bool BIG_T, int QB>
 __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a) {
   constexpr int kWaves = 8 / QB;
   constexpr int kRowsW = 32 * QB;                 // query rows per wave
+  constexpr bool kAgprO = QB > 1;                 // O^T accumulators in AGPRs
   constexpr int kQTile = kWaves * kRowsW;         // 256
   // Four K/V stages, the K tiles of all four in one array and the V^T tiles
   // in another: every operand read then addresses its stage and block with
@@ -605,6 +610,28 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
+  // With two row blocks per wave the O^T accumulators (128 registers at
+  // D = 128) live in AGPRs: the O products are written as inline asm with
+  // AGPR accumulators, while the S products stay in VGPR form for the
+  // softmax that reads them.  The compiler does not see an asm product's
+  // result latency, so every ordinary read of an accumulator waits behind a
+  // fence that first pads 24 wait states (more than the product's result
+  // latency), and every ordinary write is followed by one before the next
+  // product reads it.  The fences carry all accumulators as operands, which
+  // orders them with the reads and writes; asm statements keep their order.
+  auto acc_fence = [&](bool before_read) {
+    if constexpr (kAgprO) {
+      if (before_read) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[0][0]));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          if (before_read ? (qb | db) != 0 : !(qb == QB - 1 && db == D / 32 - 1))
+            asm volatile("" : "+a"(oacc[qb][db]));
+      if (!before_read) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[QB - 1][D / 32 - 1]));
+    }
+  };
+  acc_fence(false);
   float m_run[QB], l_run[QB];
   mfma_f32x16 mseed[QB];
 #pragma unroll
@@ -770,18 +797,20 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
   //            k-steps, K operand reads two steps ahead; the first product
   //            starts from the masked or plain seed), each k-step slot
   //            followed by an eighth of this block's softmax (per row block 2
-  //            exp2, 1 pack, 1 row-sum dot) and, at a tile's second block, one
-  //            of the next tile's transfers;
+  //            exp2, 1 pack, 1 row-sum dot) and, at a tile's first block, one
+  //            of a later tile's transfers;
   //   phase 2: O^T += V^T P^T over this block's two 16-key steps (V^T reads
   //            two ahead), with the row maxima of the next block between the
   //            products of the second half.
+  // Each phase issues the first two operand reads of the phase after it in
+  // its last two slots (the operand rings kop and vop carry them over), so no
+  // phase starts by waiting out a full LDS read.
   // Blocks a row does not see are computed and masked, so neither phase has a
   // branch inside; the only data-dependent one is the rare running-max raise.
+  mfma_bf16x8 kop[3], vop[3];
   auto phase1 = [&](int kst_, int kbn, mfma_f32x16 (&sn)[QB], const mfma_f32x16 (&sc)[QB], u32x4 (&pk)[QB][2],
-                    const TilePlan* np, int nst, int jn) {
-    mfma_bf16x8 kop[3];
-    kop[0] = kread(kst_, kbn, 0);
-    kop[1] = kread(kst_, kbn, 1);
+                    const TilePlan* np, int nst, int jn, int vst_, int vkb) {
+    // kop[0], kop[1] hold (or are loading) k-steps 0 and 1 of block kbn.
     // First k-step: the accumulator starts at -m of the row (scores come out
     // re-based), or at -inf for the keys the row does not see when the next
     // block reaches past the wave's first row's last visible key.  Deciding
@@ -808,6 +837,9 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
             sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s % 3], qfrag[qb][s], sn[qb], 0, 0, 0);
         }
       }
+      // the next phase's first two V^T operands
+      if (s == 6) vop[0] = vread(vst_, 2 * vkb, 0);
+      if (s == 7) vop[1] = vread(vst_, 2 * vkb + 1 / (D / 32), 1 % (D / 32));
       if (np && s < NDMA) fire(*np, s, nst);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {  // pair s of row block qb: 16-key half s/4, word s%4
@@ -820,20 +852,29 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto phase2 = [&](int vst_, int kb, const u32x4 (&pk)[QB][2], const mfma_f32x16 (&sn)[QB], float (&mx)[QB]) {
+  auto phase2 = [&](int vst_, int kb, const u32x4 (&pk)[QB][2], const mfma_f32x16 (&sn)[QB], float (&mx)[QB],
+                    int kst_next, int kbn_next) {
     constexpr int NR = 2 * (D / 32);  // V^T operand reads: (s2, db) = (r / (D/32), r % (D/32))
     static_assert(NR / 2 + QB <= NR, "a slot for each row block's maximum");
-    mfma_bf16x8 vop[3];
-    vop[0] = vread(vst_, 2 * kb, 0);
-    vop[1] = vread(vst_, 2 * kb + 1 / (D / 32), 1 % (D / 32));
+    static_assert(NR >= 4 && KS >= 2, "room for the next phase's first reads");
+    // vop[0], vop[1] hold (or are loading) the first two V^T operands
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int s2 = r / (D / 32), db = r % (D / 32);
       if (r + 2 < NR)
         vop[(r + 2) % 3] = vread(vst_, 2 * kb + (r + 2) / (D / 32), (r + 2) % (D / 32));
+      // the next phase's first two K operands
+      if (r == NR - 2) kop[0] = kread(kst_next, kbn_next, 0);
+      if (r == NR - 1) kop[1] = kread(kst_next, kbn_next, 1);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[r % 3], as_bf16x8(pk[qb][s2]), oacc[qb][db], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (kAgprO)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+a"(oacc[qb][db])
+                       : "v"(vop[r % 3]), "v"(as_bf16x8(pk[qb][s2])));
+        else
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[r % 3], as_bf16x8(pk[qb][s2]), oacc[qb][db], 0, 0, 0);
+      }
       // the next block's scores are complete (and past the MFMA result
       // hazard) from half way on
       if (r >= NR / 2 && r < NR / 2 + QB) mx[r - NR / 2] = row_max(sn[r - NR / 2]);
@@ -853,6 +894,7 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
       up = up || mx[qb] > m_run[qb] + kLazy;
     }
     if (__any(up)) {
+      acc_fence(true);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float m_new = mx[qb] > m_run[qb] + kLazy ? ceilf(mx[qb]) : m_run[qb];
@@ -870,6 +912,7 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mseed[qb][i] = -m_next;
       }
+      acc_fence(false);
     }
   };
 
@@ -877,13 +920,14 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
   // t = j / 2, and tile t lives in LDS stage (t - tile_lo) % 4.  Step j runs
   // phase 1 [S(j+1) products | softmax of block j] and phase 2 [PV(j)
   // products | maxima of S(j+1)], then raises the maxima if needed.  At the
-  // second block of tile t the wave first waits until tile t+1 has landed
+  // first block of tile t the wave first waits until tile t+1 has landed
   // (only tile t+2's transfers may still be out) and meets the other waves
   // at a barrier (all are past tile t-1, so its stage is free); tile t+3's
-  // transfers then go into that stage during phase 1.  Past the end the last
-  // tile is fetched again into a stage nobody reads (which keeps the count
-  // of transfers in flight the same at every wait), and the last step's
-  // next-block products are computed and dropped.
+  // transfers then go into that stage during phase 1.  Every K operand a
+  // phase 2 reads ahead (blocks of tiles t and t+1) has landed by then.  Past
+  // the end the last tile is fetched again into a stage nobody reads (which
+  // keeps the count of transfers in flight the same at every wait), and the
+  // last step's next-block products are computed and dropped.
   const int t_last = tile_hi - 1;
   mfma_f32x16 sa[QB], sb[QB];
   u32x4 pk[QB][2];
@@ -899,12 +943,14 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
     // S of the first block, with nothing to overlap
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const mfma_bf16x8 kop = kread(0, 0, s);
+      const mfma_bf16x8 k0 = kread(0, 0, s);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qfrag[qb][s], s == 0 ? mseed[qb] : sa[qb], 0, 0, 0);
+        sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qfrag[qb][s], s == 0 ? mseed[qb] : sa[qb], 0, 0, 0);
       }
     }
+    kop[0] = kread(0, 1, 0);
+    kop[1] = kread(0, 1, 1);
     float mx0[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -919,15 +965,15 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
     const int jn = t * kKTile + 32 * KB + 32;  // first key of the next block
     float mx[QB];
     if constexpr (KB == 0) {
-      phase1(cur, 1, s_nxt, s_cur, pk, nullptr, 0, jn);
-      phase2(cur, 0, pk, s_nxt, mx);
-      raise_max(s_nxt, mx);
-    } else {
       wait_vmcnt<NDMA>();
       barrier();
       const TilePlan np = plan_tile(min(t + 3, t_last));
-      phase1(nxt, 0, s_nxt, s_cur, pk, &np, fr, jn);
-      phase2(cur, 1, pk, s_nxt, mx);
+      phase1(cur, 1, s_nxt, s_cur, pk, &np, fr, jn, cur, 0);
+      phase2(cur, 0, pk, s_nxt, mx, nxt, 0);
+      raise_max(s_nxt, mx);
+    } else {
+      phase1(nxt, 0, s_nxt, s_cur, pk, nullptr, 0, jn, cur, 1);
+      phase2(cur, 1, pk, s_nxt, mx, nxt, 1);
       if (t < t_last) raise_max(s_nxt, mx);
     }
   };
@@ -950,6 +996,7 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
     }
   }
   wait_vmcnt0();
+  acc_fence(true);
 
   // ---- epilogue: lane holds O^T[d][row] of its row blocks
 #pragma unroll
@@ -1176,11 +1223,11 @@ int attn_kernel_variant(int dtype, int B, int H, int D, int T, int n_q, int num_
   (void)B; (void)H; (void)D; (void)T; (void)n_q; (void)num_cus;
   if (dtype != kBF16) return 0;
   if (const int v = launch_override(kKnobAttnKernel)) return v;
-  // 1: attn_bf16_kernel.  2: attn_bf16_pipe_kernel, the in-wave interleaved
-  // variant; it measures a few per cent slower on the Wan-1.3B layer (its
-  // vector and scalar instruction count per key tile is the larger), so it is
-  // not the default.  Both run eight waves of 32 query rows, one workgroup of
-  // 256 rows per CU.
+  // 1: attn_bf16_kernel.  2: attn_bf16_pipe_kernel with eight waves of 32
+  // query rows, the in-wave interleaved variant; it measures a few per cent
+  // slower on the Wan-1.3B layer (its vector and scalar instruction count per
+  // key tile is the larger), so it is not the default.  3: the same kernel
+  // with four waves of 64 rows.  All run one workgroup of 256 rows per CU.
   return 1;
 }
 
@@ -1234,16 +1281,19 @@ hipError_t launch_window_attn(const AttnArgs& a, int dtype, hipStream_t stream) 
   } else if (dtype == kBF16) {
     const int64_t wgs = static_cast<int64_t>((Lq + 255) / 256) * BH * a.n_splits;  // 256 query rows per workgroup
     const dim3 grid(static_cast<unsigned>(wgs));
-    const dim3 block(512);
+    const dim3 block(a.variant == 3 ? 256 : 512);
     const bool big_t = a.g.T >= kKTile;
 #define SA_LAUNCH_ATTN(DD, BT, WW) hipLaunchKernelGGL((attn_bf16_kernel<DD, BT, WW>), grid, block, 0, stream, a)
-#define SA_LAUNCH_PIPE(DD, BT) hipLaunchKernelGGL((attn_bf16_pipe_kernel<DD, BT, 1>), grid, block, 0, stream, a)
-    if (a.variant != 2) {
+#define SA_LAUNCH_PIPE(DD, BT, QQ) hipLaunchKernelGGL((attn_bf16_pipe_kernel<DD, BT, QQ>), grid, block, 0, stream, a)
+    if (a.variant == 2) {
+      if (a.g.D == 128) { if (big_t) SA_LAUNCH_PIPE(128, true, 1); else SA_LAUNCH_PIPE(128, false, 1); }
+      else { if (big_t) SA_LAUNCH_PIPE(64, true, 1); else SA_LAUNCH_PIPE(64, false, 1); }
+    } else if (a.variant == 3) {
+      if (a.g.D == 128) { if (big_t) SA_LAUNCH_PIPE(128, true, 2); else SA_LAUNCH_PIPE(128, false, 2); }
+      else { if (big_t) SA_LAUNCH_PIPE(64, true, 2); else SA_LAUNCH_PIPE(64, false, 2); }
+    } else {
       if (a.g.D == 128) { if (big_t) SA_LAUNCH_ATTN(128, true, 8); else SA_LAUNCH_ATTN(128, false, 8); }
       else { if (big_t) SA_LAUNCH_ATTN(64, true, 8); else SA_LAUNCH_ATTN(64, false, 8); }
-    } else {
-      if (a.g.D == 128) { if (big_t) SA_LAUNCH_PIPE(128, true); else SA_LAUNCH_PIPE(128, false); }
-      else { if (big_t) SA_LAUNCH_PIPE(64, true); else SA_LAUNCH_PIPE(64, false); }
     }
 #undef SA_LAUNCH_PIPE
 #undef SA_LAUNCH_ATTN

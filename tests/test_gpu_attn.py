@@ -81,7 +81,7 @@ def test_cfg1_tiny_f32_stream():
             _check(gs, q, o, mask == swk.SA_MASK_FRAME_CAUSAL, what=f"cfg1 frame {f} mask {mask}")
 
 
-@pytest.mark.parametrize("splits,kernel", [(None, None), ("1", None), ("5", None), (None, "2"), ("3", "2")])
+@pytest.mark.parametrize("splits,kernel", [(None, None), ("1", None), ("5", None), (None, "2"), ("3", "2"), (None, "3"), ("3", "3")])
 def test_cfg2_wan_layer_stream(splits, kernel):
     """Wan-1.3B layer, bf16, 3 sink + 9 local, 40 frames; checks while filling and in steady state."""
     swk = _swk()
@@ -165,7 +165,7 @@ def test_stores_start_as_nan_bits(grid):
     w = dataclasses.replace(wl.WORKLOADS[2], name="bf16-nan-fill", cfg=55, n_heads=4 if grid == (4, 10) else 12,
                             grid=grid, frames=6, batch=2 if grid == (4, 10) else 1)
     rows = None if grid == (4, 10) else sample_rows(w.tokens_per_frame, w.tokens_per_frame, n=48, seed=6)
-    for kernel in ("1", "2"):
+    for kernel in ("1", "2", "3"):
         gs = GpuStream(w)
         gs.cache.k_store.view(torch.int16).fill_(-1)   # bf16 bits 0xffff: a NaN
         gs.cache.v_store.view(torch.int16).fill_(-1)
@@ -271,7 +271,7 @@ def _check_sharp(gs, q, o, causal, rows, scale, what):
     return sigma
 
 
-@pytest.mark.parametrize("splits,kernel", [(None, None), ("1", None), (None, "2")])
+@pytest.mark.parametrize("splits,kernel", [(None, None), ("1", None), (None, "2"), (None, "3")])
 def test_sharp_softmax_score_std_3(splits, kernel):
     """Unscaled N(0,1) q and k with scale 0.25: scores of standard deviation ~2.8 nats at the Wan-1.3B layer
     shapes, so a few keys dominate each row.  Checked while filling (frame 3) and after the first eviction
@@ -376,7 +376,7 @@ def test_cfg3_lol_jitter_long_positions():
             log(f"  rel_l2 {rel:.2e} max_abs {mx:.2e}")
 
 
-@pytest.mark.parametrize("kernel", [None, "2"])
+@pytest.mark.parametrize("kernel", [None, "2", "3"])
 def test_cfg5_chunked_causal_batched(kernel):
     """B = 4 streams, 3-frame query chunks, frame-causal inside the chunk, sigma = 0.8 (layer 29 seeds)."""
     swk = _swk()
@@ -406,7 +406,7 @@ def test_cfg5_chunked_causal_batched(kernel):
     (128, (44, 42, 42), (1, 8), 0, 64, 1, 1, 80),  # the largest window (64 frames), no sinks
     (128, (44, 42, 42), (5, 40), 3, 9, 1, 1, 14),  # T = 200: key tiles straddle frames
 ])
-@pytest.mark.parametrize("kernel", ["1", "2"])
+@pytest.mark.parametrize("kernel", ["1", "2", "3"])
 def test_small_shapes_bf16(D, dims, grid, n_sink, n_local, n_q, mask, frames, kernel):
     w = wl.Workload("edge", 42, batch=2, n_heads=3, head_dim=D, dims=dims, grid=grid, n_sink=n_sink,
                     n_local=n_local, chunk=n_q, frames=frames, dtype="bf16", sigma=0.8)
@@ -442,7 +442,7 @@ def test_values_one_gives_one_and_runs_are_deterministic():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("kernel", ["1", "2"])
+@pytest.mark.parametrize("kernel", ["1", "2", "3"])
 def test_running_max_raises(kernel):
     """Scores that grow along the key sequence: keys of frame f scaled by (1 + f), so later tiles keep
     exceeding the running max and the max is raised tile after tile.  Every row vs the oracle (score

@@ -42,7 +42,7 @@ SMALL = wl.Workload("mass-small", 51, batch=2, n_heads=4, head_dim=128, dims=(44
                     n_sink=2, n_local=3, chunk=1, frames=8, dtype="bf16", sigma=0.8)
 
 
-@pytest.mark.parametrize("kernel", ["1", "2"])
+@pytest.mark.parametrize("kernel", ["1", "2", "3"])
 def test_sink_mass_small_stream(kernel):
     """Every frame from the first (query frames that are sinks: mass 1) through eviction; both masks;
     unscaled N(0,1) queries and keys so the softmax is sharp and the mass varies."""
@@ -69,7 +69,7 @@ def test_sink_mass_chunks_b2():
         _check_mass(gs, q, 3, swk.SA_MASK_FRAME_CAUSAL, what=f"chunk at {f0}")
 
 
-@pytest.mark.parametrize("splits,kernel", [(None, None), ("1", None), ("5", None), (None, "2")])
+@pytest.mark.parametrize("splits,kernel", [(None, None), ("1", None), ("5", None), (None, "2"), (None, "3")])
 def test_sink_mass_wan_layer(splits, kernel):
     """Wan-1.3B layer in steady state (3 sinks + 9 local, 18720 keys), sampled rows, all heads,
     LoL jitter sigma = 0.8; launch shapes forced as for the attention."""

@@ -81,7 +81,7 @@ def test_host_launch_override_validation():
     """sa_set_launch_override accepts each knob's set (0 = automatic) and rejects the rest."""
     swk = _swk()
     L = swk.lib()
-    for knob, good, bad in ((swk.SA_KNOB_ATTN_KERNEL, (0, 1, 2), (3, 4, 8, -1)),
+    for knob, good, bad in ((swk.SA_KNOB_ATTN_KERNEL, (0, 1, 2, 3), (4, 8, -1)),
                             (swk.SA_KNOB_ATTN_SPLITS, (0, 1, 3, 16), (-1, 17)),
                             (swk.SA_KNOB_PROJ_TILE, (0, 1, 2, 3, 4), (-1, 5))):
         for v in good:
