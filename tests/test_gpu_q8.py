@@ -161,13 +161,15 @@ SMALL = wl.Workload("q8-small", 48, batch=2, n_heads=4, head_dim=128, dims=(44, 
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
-@pytest.mark.parametrize("cache", ["bf16", "fp8"])
-def test_project_append_q8_stream(qtype, cache):
+@pytest.mark.parametrize("cache,hidden", [("bf16", 256), ("fp8", 256), ("bf16", 192)])
+def test_project_append_q8_stream(qtype, cache, hidden):
     """8-bit per-frame projections streamed in chunks of 1-3 frames (sinks, ring wrap, eviction): q, the
-    stored K and V and the slot map vs the oracle on the dequantized operands; an e4m3 cache too."""
+    stored K and V and the slot map vs the oracle on the dequantized operands; an e4m3 cache too.  Hidden
+    256 is four 64-byte reduction slices, hidden 192 three (a whole number of register-buffer rounds)."""
+    import dataclasses
     import torch
     swk = _swk()
-    w = SMALL
+    w = dataclasses.replace(SMALL, hidden=hidden)
     eps = wl.head_jitter(w)
     gs = GpuStream(w, eps=eps)
     if cache == "fp8":
