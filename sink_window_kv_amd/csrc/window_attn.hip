@@ -797,20 +797,22 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
   //            k-steps, K operand reads two steps ahead; the first product
   //            starts from the masked or plain seed), each k-step slot
   //            followed by an eighth of this block's softmax (per row block 2
-  //            exp2, 1 pack, 1 row-sum dot) and, at a tile's first block, one
-  //            of a later tile's transfers;
+  //            exp2, 1 pack, 1 row-sum dot) and one of a later tile's
+  //            transfers (half of them at each block of a tile);
   //   phase 2: O^T += V^T P^T over this block's two 16-key steps (V^T reads
   //            two ahead), with the row maxima of the next block between the
   //            products of the second half.
-  // Each phase issues the first two operand reads of the phase after it in
-  // its last two slots (the operand rings kop and vop carry them over), so no
-  // phase starts by waiting out a full LDS read.
+  // Operand reads run kLA products ahead, through rings of kLA + 1, and each
+  // phase issues the first kLA operand reads of the phase after it in its
+  // last kLA slots, so no phase starts by waiting out a full LDS read.
   // Blocks a row does not see are computed and masked, so neither phase has a
   // branch inside; the only data-dependent one is the rare running-max raise.
-  mfma_bf16x8 kop[3], vop[3];
+  constexpr int kLA = 4, kRing = kLA + 1;
+  static_assert(kLA <= KS && kLA <= 4 * (D / 32) && kLA <= 8, "read-ahead within a phase");
+  mfma_bf16x8 kop[kRing], vop[kRing];
   auto phase1 = [&](int kst_, int kbn, mfma_f32x16 (&sn)[QB], const mfma_f32x16 (&sc)[QB], u32x4 (&pk)[QB][2],
-                    const TilePlan* np, int nst, int jn, int vst_, int vkb) {
-    // kop[0], kop[1] hold (or are loading) k-steps 0 and 1 of block kbn.
+                    const TilePlan* np, int nst, int u0, int nu, int jn, int vst_, int vkb) {
+    // kop[0 .. kLA-1] hold (or are loading) k-steps 0 .. kLA-1 of block kbn.
     // First k-step: the accumulator starts at -m of the row (scores come out
     // re-based), or at -inf for the keys the row does not see when the next
     // block reaches past the wave's first row's last visible key.  Deciding
@@ -830,17 +832,19 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       if (s < KS) {
-        if (s + 2 < KS) kop[(s + 2) % 3] = kread(kst_, kbn, s + 2);
+        if (s + kLA < KS) kop[(s + kLA) % kRing] = kread(kst_, kbn, s + kLA);
         if (s > 0) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s % 3], qfrag[qb][s], sn[qb], 0, 0, 0);
+            sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s % kRing], qfrag[qb][s], sn[qb], 0, 0, 0);
         }
       }
-      // the next phase's first two V^T operands
-      if (s == 6) vop[0] = vread(vst_, 2 * vkb, 0);
-      if (s == 7) vop[1] = vread(vst_, 2 * vkb + 1 / (D / 32), 1 % (D / 32));
-      if (np && s < NDMA) fire(*np, s, nst);
+      // the next phase's first kLA V^T operands
+      if (s >= 8 - kLA) {
+        const int i = s - (8 - kLA);
+        vop[i] = vread(vst_, 2 * vkb + i / (D / 32), i % (D / 32));
+      }
+      if (np && s < nu) fire(*np, u0 + s, nst);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {  // pair s of row block qb: 16-key half s/4, word s%4
         const int s2 = s >> 2, w = s & 3;
@@ -856,24 +860,22 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
                     int kst_next, int kbn_next) {
     constexpr int NR = 2 * (D / 32);  // V^T operand reads: (s2, db) = (r / (D/32), r % (D/32))
     static_assert(NR / 2 + QB <= NR, "a slot for each row block's maximum");
-    static_assert(NR >= 4 && KS >= 2, "room for the next phase's first reads");
-    // vop[0], vop[1] hold (or are loading) the first two V^T operands
+    // vop[0 .. kLA-1] hold (or are loading) the first kLA V^T operands
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int s2 = r / (D / 32), db = r % (D / 32);
-      if (r + 2 < NR)
-        vop[(r + 2) % 3] = vread(vst_, 2 * kb + (r + 2) / (D / 32), (r + 2) % (D / 32));
-      // the next phase's first two K operands
-      if (r == NR - 2) kop[0] = kread(kst_next, kbn_next, 0);
-      if (r == NR - 1) kop[1] = kread(kst_next, kbn_next, 1);
+      if (r + kLA < NR)
+        vop[(r + kLA) % kRing] = vread(vst_, 2 * kb + (r + kLA) / (D / 32), (r + kLA) % (D / 32));
+      // the next phase's first kLA K operands
+      if (r >= NR - kLA) kop[r - (NR - kLA)] = kread(kst_next, kbn_next, r - (NR - kLA));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if constexpr (kAgprO)
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                        : "+a"(oacc[qb][db])
-                       : "v"(vop[r % 3]), "v"(as_bf16x8(pk[qb][s2])));
+                       : "v"(vop[r % kRing]), "v"(as_bf16x8(pk[qb][s2])));
         else
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[r % 3], as_bf16x8(pk[qb][s2]), oacc[qb][db], 0, 0, 0);
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[r % kRing], as_bf16x8(pk[qb][s2]), oacc[qb][db], 0, 0, 0);
       }
       // the next block's scores are complete (and past the MFMA result
       // hazard) from half way on
@@ -923,11 +925,12 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
   // first block of tile t the wave first waits until tile t+1 has landed
   // (only tile t+2's transfers may still be out) and meets the other waves
   // at a barrier (all are past tile t-1, so its stage is free); tile t+3's
-  // transfers then go into that stage during phase 1.  Every K operand a
-  // phase 2 reads ahead (blocks of tiles t and t+1) has landed by then.  Past
-  // the end the last tile is fetched again into a stage nobody reads (which
-  // keeps the count of transfers in flight the same at every wait), and the
-  // last step's next-block products are computed and dropped.
+  // transfers then go into that stage during the phase 1 of both blocks.
+  // Every K operand a phase 2 reads ahead (blocks of tiles t and t+1) has
+  // landed by then.  Past the end the last tile is fetched again into a
+  // stage nobody reads (which keeps the count of transfers in flight the
+  // same at every wait), and the last step's next-block products are
+  // computed and dropped.
   const int t_last = tile_hi - 1;
   mfma_f32x16 sa[QB], sb[QB];
   u32x4 pk[QB][2];
@@ -949,8 +952,8 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
         sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qfrag[qb][s], s == 0 ? mseed[qb] : sa[qb], 0, 0, 0);
       }
     }
-    kop[0] = kread(0, 1, 0);
-    kop[1] = kread(0, 1, 1);
+#pragma unroll
+    for (int i = 0; i < kLA; ++i) kop[i] = kread(0, 1, i);
     float mx0[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -959,7 +962,10 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
     }
     raise_max(sa, mx0);
   }
-  // step over block (t, KB): stage cur holds tile t, nxt tile t+1, fr receives tile t+3
+  // step over block (t, KB): stage cur holds tile t, nxt tile t+1, fr receives
+  // tile t+3, whose transfers are split between the tile's two steps
+  constexpr int kFire0 = NDMA / 2;
+  TilePlan np_t3;
   auto step = [&](auto kb_c, int t, mfma_f32x16 (&s_cur)[QB], mfma_f32x16 (&s_nxt)[QB], int cur, int nxt, int fr) {
     constexpr int KB = decltype(kb_c)::value;
     const int jn = t * kKTile + 32 * KB + 32;  // first key of the next block
@@ -967,12 +973,12 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
     if constexpr (KB == 0) {
       wait_vmcnt<NDMA>();
       barrier();
-      const TilePlan np = plan_tile(min(t + 3, t_last));
-      phase1(cur, 1, s_nxt, s_cur, pk, &np, fr, jn, cur, 0);
+      np_t3 = plan_tile(min(t + 3, t_last));
+      phase1(cur, 1, s_nxt, s_cur, pk, &np_t3, fr, 0, kFire0, jn, cur, 0);
       phase2(cur, 0, pk, s_nxt, mx, nxt, 0);
       raise_max(s_nxt, mx);
     } else {
-      phase1(nxt, 0, s_nxt, s_cur, pk, nullptr, 0, jn, cur, 1);
+      phase1(nxt, 0, s_nxt, s_cur, pk, &np_t3, fr, kFire0, NDMA - kFire0, jn, cur, 1);
       phase2(cur, 1, pk, s_nxt, mx, nxt, 1);
       if (t < t_last) raise_max(s_nxt, mx);
     }
