@@ -617,8 +617,10 @@ __global__ void __launch_bounds__(512 / QB, 1) attn_bf16_pipe_kernel(AttnArgs a)
   // result latency, so every ordinary read of an accumulator waits behind a
   // fence that first pads 24 wait states (more than the product's result
   // latency), and every ordinary write is followed by one before the next
-  // product reads it.  The fences carry all accumulators as operands, which
-  // orders them with the reads and writes; asm statements keep their order.
+  // product reads it.  A fence is one asm statement per accumulator, with the
+  // padding in the first (before reads) or the last (after writes); each
+  // statement takes its accumulator as an operand, which orders it with that
+  // accumulator's reads and writes, and asm statements keep their order.
   auto acc_fence = [&](bool before_read) {
     if constexpr (kAgprO) {
       if (before_read) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[0][0]));
