@@ -42,21 +42,24 @@ def _both(cache, q, n_q, mask, scale=0.0):
     return nbytes, o_ref, o_na
 
 
-def test_noalloc_matches_workspace_entry_point_two_calls():
+@pytest.mark.parametrize("kernel", [None, "3"])
+def test_noalloc_matches_workspace_entry_point_two_calls(kernel):
+    """The default attention kernel, and the 64-row pipelined variant (its O accumulators in AGPRs)."""
     swk = _swk()
     # call 1: the Wan-1.3B layer in steady state (1560 queries over 12 frames, 3 key splits: 29.2 MB of partials)
     w1 = wl.WORKLOADS[2]
-    log("noalloc call 1: Wan-1.3B layer, frame 13")
+    log(f"noalloc call 1: Wan-1.3B layer, frame 13, kernel {kernel}")
     rope1, c1 = _filled_cache(w1, 14, 0)
     q1 = to_dev(wl.frame_qkv(w1, 13, tensor=wl.TENSOR_Q, scale=1.0), "bf16")
-    n1, ref1, got1 = _both(c1, q1, 1, swk.SA_MASK_FRAME_CAUSAL)
+    with launch_override(kernel=kernel):
+        n1, ref1, got1 = _both(c1, q1, 1, swk.SA_MASK_FRAME_CAUSAL)
     assert n1 > 0, "the first call must use the scratch (key splits)"
     assert torch.equal(got1, ref1), "call 1: noalloc output differs from sa_window_attn"
     # call 2: smaller (2 heads, 200 tokens per frame, a 2-frame frame-causal chunk, 5 forced key splits)
     w2 = dataclasses.replace(wl.WORKLOADS[3], name="noalloc-small", n_heads=2, grid=(10, 20), n_sink=1,
                              n_local=4, sigma=0.8)
-    log("noalloc call 2: H=2, T=200, 2-frame chunk, 5 splits")
-    with launch_override(splits=5):
+    log(f"noalloc call 2: H=2, T=200, 2-frame chunk, 5 splits, kernel {kernel}")
+    with launch_override(kernel=kernel, splits=5):
         rope2, c2 = _filled_cache(w2, 7, 1)
         q2 = to_dev(np.concatenate([wl.frame_qkv(w2, f, layer=1, tensor=wl.TENSOR_Q, scale=1.0)
                                     for f in (5, 6)], axis=1), "bf16")
@@ -66,7 +69,8 @@ def test_noalloc_matches_workspace_entry_point_two_calls():
     assert torch.isfinite(got2.float()).all()
     # the first cache again after the smaller call (the scratch keeps the last call's bytes)
     o_again = torch.empty_like(q1)
-    swk.sa_window_attn_noalloc(c1, q1, o_again, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL)
+    with launch_override(kernel=kernel):
+        swk.sa_window_attn_noalloc(c1, q1, o_again, 1, 0.0, swk.SA_MASK_FRAME_CAUSAL)
     torch.cuda.synchronize()
     assert torch.equal(o_again, ref1)
     for c, r in ((c1, rope1), (c2, rope2)):
